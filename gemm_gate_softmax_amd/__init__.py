@@ -5,6 +5,8 @@ declared in ``include/moe.h``).  ``gemm_gate_softmax_amd.ops`` is the thin ctype
 over it; importing this package does not load the library, calling an op does, and fails
 loudly if it has not been built.
 """
+import importlib
+
 from . import workloads  # noqa: F401
 
 __all__ = ["workloads", "ops"]
@@ -12,6 +14,5 @@ __all__ = ["workloads", "ops"]
 
 def __getattr__(name):
     if name == "ops":
-        from . import ops
-        return ops
+        return importlib.import_module(".ops", __name__)
     raise AttributeError(name)

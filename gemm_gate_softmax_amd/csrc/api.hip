@@ -1,0 +1,181 @@
+// api.hip -- the C ABI of libmoe.so (declared in include/moe.h): argument validation,
+// workspace carving and the stage chain.  No device memory is allocated here and nothing
+// synchronises; every launch goes to the caller's stream.
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dt(moe_dtype_t dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+moe_status_t check_route(int T, int E, int k) {
+    if (T < 0 || E < 1 || k < 1) return MOE_ERR_INVALID_VALUE;
+    if (E > MOE_E_MAX || k > MOE_K_MAX || k > E) return MOE_ERR_UNSUPPORTED;
+    if ((long long)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status_t check_dim(int d) {
+    if (d <= 0) return MOE_ERR_INVALID_VALUE;
+    if (d % 64 != 0) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status_t check_ptrs(std::initializer_list<const void*> ps) {
+    for (const void* p : ps) {
+        if (!p) return MOE_ERR_INVALID_VALUE;
+        if (!aligned16(p)) return MOE_ERR_MISALIGNED;
+    }
+    return MOE_OK;
+}
+
+moe_status_t launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+#define MOE_TRY(expr)                        \
+    do {                                     \
+        const moe_status_t st_ = (expr);     \
+        if (st_ != MOE_OK) return st_;       \
+    } while (0)
+
+size_t gate_ws(int T, int E) { return round_up((size_t)T * E * sizeof(float)); }
+size_t pft_ws(int T, int k, int E) { return round_up(moe::pft_ws_bytes((long long)T * k, E)); }
+size_t gemm_ws(long long N, int E) { return round_up(moe::gemm_ws_bytes(N, E)); }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+MOE_API size_t moe_workspace_bytes(int kind, int T, int H, int E, int F, int k, moe_dtype_t dt) {
+    (void)H; (void)F;
+    if (!valid_dt(dt) || check_route(T, E, k) != MOE_OK) return 0;
+    switch (kind) {
+        case MOE_WS_GATE: return gate_ws(T, E);
+        case MOE_WS_PFT: return pft_ws(T, k, E);
+        case MOE_WS_GEMM: return gemm_ws((long long)T * k, E);
+        case MOE_WS_LAYER: return pft_ws(T, k, E) + gate_ws(T, E) + gemm_ws((long long)T * k, E);
+        default: return 0;
+    }
+}
+
+MOE_API const char* moe_status_string(moe_status_t s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_VALUE: return "MOE_ERR_INVALID_VALUE: argument out of range or NULL";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape outside the supported limits";
+        case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED: device pointer not 16-byte aligned";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: the HIP runtime refused a kernel launch";
+        default: return "unknown moe_status_t";
+    }
+}
+
+MOE_API moe_status_t moe_gate_topk(moe_dtype_t dt, int T, int H, int E, int k, const void* x,
+                                   const void* wg, const float* bias, int32_t* top_experts,
+                                   float* top_weights, void* ws, size_t ws_bytes, void* stream) {
+    if (!valid_dt(dt)) return MOE_ERR_INVALID_VALUE;
+    MOE_TRY(check_route(T, E, k));
+    MOE_TRY(check_dim(H));
+    if (T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x, wg, top_experts, top_weights, ws}));
+    if (bias && !aligned16(bias)) return MOE_ERR_MISALIGNED;
+    if (ws_bytes < gate_ws(T, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    float* logits = static_cast<float*>(ws);
+    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, bias, logits, as_stream(stream))));
+    return launched(moe::launch_topk(T, E, k, logits, top_experts, top_weights, as_stream(stream)));
+}
+
+MOE_API moe_status_t moe_pft_build(int T, int k, int E, const int32_t* top_experts,
+                                   int32_t* counts, int32_t* offsets, int32_t* token_ids,
+                                   int32_t* expert_ids, int32_t* dest_pos, void* ws,
+                                   size_t ws_bytes, void* stream) {
+    MOE_TRY(check_route(T, E, k));
+    MOE_TRY(check_ptrs({counts, offsets, ws}));
+    if (T > 0) MOE_TRY(check_ptrs({top_experts, token_ids, expert_ids, dest_pos}));
+    if (ws_bytes < pft_ws(T, k, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return launched(moe::launch_pft(T, k, E, top_experts, counts, offsets, token_ids, expert_ids,
+                                    dest_pos, ws, as_stream(stream)));
+}
+
+MOE_API moe_status_t moe_dispatch(moe_dtype_t dt, int T, int k, int H, const void* x,
+                                  const int32_t* dest_pos, void* xd, void* stream) {
+    if (!valid_dt(dt)) return MOE_ERR_INVALID_VALUE;
+    if (T < 0 || k < 1) return MOE_ERR_INVALID_VALUE;
+    if (k > MOE_K_MAX || (long long)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(check_dim(H));
+    if (T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x, dest_pos, xd}));
+    return launched(moe::launch_dispatch(dt, T, k, H, x, dest_pos, xd, as_stream(stream)));
+}
+
+MOE_API moe_status_t moe_grouped_gemm_swiglu(moe_dtype_t dt, int N, int E, int H, int F,
+                                             const void* xd, const int32_t* offsets,
+                                             const void* w1, const void* w3, const void* w2,
+                                             void* h, void* y, void* ws, size_t ws_bytes,
+                                             void* stream) {
+    if (!valid_dt(dt)) return MOE_ERR_INVALID_VALUE;
+    if (N < 0 || E < 1) return MOE_ERR_INVALID_VALUE;
+    if (E > MOE_E_MAX) return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(check_dim(H));
+    MOE_TRY(check_dim(F));
+    if (N == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({xd, offsets, w1, w3, w2, h, y, ws}));
+    if (ws_bytes < gemm_ws(N, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return launched(moe::launch_grouped_gemm(dt, N, E, H, F, xd, offsets, w1, w3, w2, h, y, ws,
+                                             as_stream(stream)));
+}
+
+MOE_API moe_status_t moe_combine(moe_dtype_t dt, int T, int k, int H, const void* y,
+                                 const int32_t* dest_pos, const float* top_weights, void* out,
+                                 void* stream) {
+    if (!valid_dt(dt)) return MOE_ERR_INVALID_VALUE;
+    if (T < 0 || k < 1) return MOE_ERR_INVALID_VALUE;
+    if (k > MOE_K_MAX || (long long)T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(check_dim(H));
+    if (T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({y, dest_pos, top_weights, out}));
+    return launched(moe::launch_combine(dt, T, k, H, y, dest_pos, top_weights, out,
+                                        as_stream(stream)));
+}
+
+MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k,
+                                       const void* x, const void* wg, const float* bias,
+                                       const void* w1, const void* w3, const void* w2,
+                                       void* out, const moe_layer_bufs* b, void* ws,
+                                       size_t ws_bytes, void* stream) {
+    if (!valid_dt(dt) || !b) return MOE_ERR_INVALID_VALUE;
+    MOE_TRY(check_route(T, E, k));
+    MOE_TRY(check_dim(H));
+    MOE_TRY(check_dim(F));
+    if (T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x, wg, w1, w3, w2, out, ws, b->top_experts, b->top_weights, b->counts,
+                        b->offsets, b->token_ids, b->expert_ids, b->dest_pos, b->xd, b->h, b->y}));
+    if (bias && !aligned16(bias)) return MOE_ERR_MISALIGNED;
+    const size_t need_pft = pft_ws(T, k, E), need_gate = gate_ws(T, E);
+    const long long N = (long long)T * k;
+    if (ws_bytes < need_pft + need_gate + gemm_ws(N, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    char* w = static_cast<char*>(ws);
+    void* ws_pft = w;                       // error word stays at byte 0
+    float* logits = reinterpret_cast<float*>(w + need_pft);
+    void* ws_gemm = w + need_pft + need_gate;
+    const hipStream_t s = as_stream(stream);
+    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, bias, logits, s)));
+    MOE_TRY(launched(moe::launch_topk(T, E, k, logits, b->top_experts, b->top_weights, s)));
+    MOE_TRY(launched(moe::launch_pft(T, k, E, b->top_experts, b->counts, b->offsets, b->token_ids,
+                                     b->expert_ids, b->dest_pos, ws_pft, s)));
+    MOE_TRY(launched(moe::launch_dispatch(dt, T, k, H, x, b->dest_pos, b->xd, s)));
+    MOE_TRY(launched(moe::launch_grouped_gemm(dt, (int)N, E, H, F, b->xd, b->offsets, w1, w3, w2,
+                                              b->h, b->y, ws_gemm, s)));
+    return launched(moe::launch_combine(dt, T, k, H, b->y, b->dest_pos, b->top_weights, out, s));
+}

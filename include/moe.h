@@ -1,0 +1,171 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the forward pass of one expert-specialised MoE layer on an
+ * AMD MI355X (gfx950) GPU, as five stages plus the whole chain.
+ *
+ * The stages follow the X-MoE review's training pipeline (web page "X-MoE:
+ * 在HPC平台上实现新兴混合专家架构的可扩展训练", section 三 技术架构, 训练流程 steps 1-3, 5
+ * and 6) with its padding-free token buffers ("PFT": token_ids / expert_ids / per-expert
+ * counts, 模型组件 table; O(B*H) rows with no E*C capacity, PFT复杂度分析), and the
+ * single-device share of the DMoE operator of the FlashDMoE blog (section 1.1: gate, send
+ * tokens to experts, expert compute, weighted merge back).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named x, wg, w1, ... are DEVICE pointers owned by the caller.  The library
+ *     never allocates or frees device memory, never synchronises, and enqueues all work on
+ *     `stream` (a hipStream_t; NULL = the default stream).  Calls are asynchronous and can
+ *     be captured into a HIP graph (no memset nodes, no host reads of device data).
+ *   - Row-major layouts, weights as nn.Linear ([out][in]):  x [T][H], wg [E][H],
+ *     bias [E] (fp32), w1 and w3 [E][F][H] (SwiGLU gate and up), w2 [E][H][F] (down).
+ *     N = T*k is the number of routed rows.
+ *   - dt selects the storage type of x, wg, w1, w3, w2, xd, h, y and out: MOE_F32 (fp32) or
+ *     MOE_BF16 (bf16).  Logits, routing weights and every accumulation are fp32.
+ *   - Limits: T >= 0 (T == 0 is a successful no-op), 1 <= k <= MOE_K_MAX, k <= E,
+ *     1 <= E <= MOE_E_MAX, H and F positive multiples of 64, N < 2^31.  Every device
+ *     pointer must be 16-byte aligned.
+ *   - The returned status covers host-side validation and launch errors only; a fault in
+ *     a kernel surfaces at the caller's next synchronisation.  Invalid arguments are
+ *     rejected before anything is enqueued.
+ *   - Workspaces are caller-owned device buffers of at least moe_workspace_bytes() bytes.
+ *     Their content between calls is scratch, except the error word described at
+ *     moe_pft_build.  Concurrent calls must not share a workspace.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_K_MAX 64
+#define MOE_E_MAX 1024
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_VALUE = 1,       /* a size or pointer argument is out of range / NULL */
+    MOE_ERR_UNSUPPORTED = 2,         /* a shape outside the limits above */
+    MOE_ERR_MISALIGNED = 3,          /* a device pointer is not 16-byte aligned */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < moe_workspace_bytes(...) */
+    MOE_ERR_LAUNCH = 5               /* the HIP runtime refused a launch */
+} moe_status_t;
+
+/* Which call a workspace is for (argument of moe_workspace_bytes). */
+typedef enum {
+    MOE_WS_GATE = 0,
+    MOE_WS_PFT = 1,
+    MOE_WS_GEMM = 2,
+    MOE_WS_LAYER = 3
+} moe_workspace_kind_t;
+
+/* Bytes of workspace a call needs for these sizes (0 for unsupported arguments).  Sizes
+ * that do not matter to a call are ignored (e.g. H and F for MOE_WS_PFT). */
+size_t moe_workspace_bytes(int kind, int T, int H, int E, int F, int k, moe_dtype_t dt);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_status_string(moe_status_t status);
+
+/*
+ * Top-k softmax gate (X-MoE review, 训练流程 step 2: gating produced straight in buffer
+ * form, no dense dispatch mask; FSMoE report, 第三部分 item 1, Gating Function module).
+ *   logit[t][e]        = sum_h x[t][h] * wg[e][h] + bias[e]          (fp32 accumulate)
+ *   top_experts[t][j]  = the j-th expert in the order (logit desc, expert id asc), j < k
+ *   top_weights[t][j]  = softmax(logit[t])[pick j] renormalised over the k picks
+ *                      = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)
+ * bias may be NULL (no bias).  Outputs: top_experts [T][k] int32, top_weights [T][k] fp32.
+ * ws: moe_workspace_bytes(MOE_WS_GATE, ...) bytes (holds the fp32 logits).
+ */
+moe_status_t moe_gate_topk(moe_dtype_t dt, int T, int H, int E, int k, const void *x,
+                           const void *wg, const float *bias, int32_t *top_experts,
+                           float *top_weights, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Padding-free token buffers (X-MoE review, 训练流程 step 1: flatten top_experts and sort
+ * it into token_ids and expert_ids; 模型组件: token_ids, expert_ids and the per-expert
+ * counts "num_ids").  With flat index i = t*k + j and e = top_experts[i]:
+ *   counts[e]  = #{ i : top_experts[i] == e },  offsets = exclusive scan, offsets[E] = N
+ *   position(i) = offsets[e] + #{ i' < i : top_experts[i'] == e }   (stable sort by expert)
+ *   token_ids[position(i)] = t,  expert_ids[position(i)] = e,  dest_pos[t][j] = position(i)
+ * Every one of the N rows is assigned exactly once: no capacity, no padding rows.
+ * Outputs (device, int32): counts [E], offsets [E+1], token_ids [N], expert_ids [N],
+ * dest_pos [T][k].
+ * ws: moe_workspace_bytes(MOE_WS_PFT, ...) bytes.  After the call completes, the int32 at
+ * byte 0 of ws holds the number of entries of top_experts outside [0, E); when it is
+ * non-zero those entries get dest_pos -1 and the other outputs are incomplete.
+ */
+moe_status_t moe_pft_build(int T, int k, int E, const int32_t *top_experts, int32_t *counts,
+                           int32_t *offsets, int32_t *token_ids, int32_t *expert_ids,
+                           int32_t *dest_pos, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Padding-free dispatch (X-MoE review, 训练流程 step 3; FlashDMoE blog, section 5: only the
+ * routed tokens are moved, no zero-filled rows):  xd[dest_pos[t][j]] = x[t]  for all t, j.
+ * A bit-exact row copy; x [T][H] -> xd [N][H].  dest_pos must be a permutation of [0, N)
+ * as produced by moe_pft_build.
+ */
+moe_status_t moe_dispatch(moe_dtype_t dt, int T, int k, int H, const void *x,
+                          const int32_t *dest_pos, void *xd, void *stream);
+
+/*
+ * Expert computation over the uneven per-expert segments (X-MoE review, 训练流程 step 5:
+ * one GEMM per expert on its own rows; FlashDMoE blog, section 5: only local padding to
+ * the tile shape, never to a capacity).  Rows p in [offsets[e], offsets[e+1]) use expert e:
+ *   h[p][f] = silu(a) * g,   a = sum_c xd[p][c] * w1[e][f][c],  g = sum_c xd[p][c] * w3[e][f][c]
+ *   y[p][c] = sum_f h[p][f] * w2[e][c][f],      silu(a) = a / (1 + exp(-a))
+ * h is rounded once to the storage type and that rounded h feeds the second product.
+ * xd [N][H], offsets [E+1] (device, as from moe_pft_build), h [N][F], y [N][H].
+ * Experts with no rows cost nothing.  ws: moe_workspace_bytes(MOE_WS_GEMM, ...) bytes
+ * (holds the device-built tile table; sized from N = T*k and E).
+ */
+moe_status_t moe_grouped_gemm_swiglu(moe_dtype_t dt, int N, int E, int H, int F,
+                                     const void *xd, const int32_t *offsets, const void *w1,
+                                     const void *w3, const void *w2, void *h, void *y,
+                                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Padding-free weighted combine (X-MoE review, 训练流程 step 6; FlashDMoE blog, section 1.1:
+ * expert results are merged back with the gate weights):
+ *   out[t][c] = sum_{j=0}^{k-1} top_weights[t][j] * y[dest_pos[t][j]][c]
+ * accumulated in fp32 in ascending j, rounded once to the storage type.  Deterministic
+ * (token-major gather, no atomics).  y [N][H], dest_pos [T][k], top_weights [T][k] fp32,
+ * out [T][H].
+ */
+moe_status_t moe_combine(moe_dtype_t dt, int T, int k, int H, const void *y,
+                         const int32_t *dest_pos, const float *top_weights, void *out,
+                         void *stream);
+
+/* Caller-owned intermediates of moe_layer_forward (device pointers, sizes as above). */
+typedef struct moe_layer_bufs {
+    int32_t *top_experts; /* [T][k] */
+    float *top_weights;   /* [T][k] */
+    int32_t *counts;      /* [E]    */
+    int32_t *offsets;     /* [E+1]  */
+    int32_t *token_ids;   /* [N]    */
+    int32_t *expert_ids;  /* [N]    */
+    int32_t *dest_pos;    /* [T][k] */
+    void *xd;             /* [N][H] */
+    void *h;              /* [N][F] */
+    void *y;              /* [N][H] */
+} moe_layer_bufs;
+
+/*
+ * The whole layer forward: gate -> buffers -> dispatch -> experts -> combine, each stage
+ * exactly as the entry point of the same name, enqueued back to back on `stream` with no
+ * host synchronisation.  x [T][H] -> out [T][H]; intermediates land in *bufs (every
+ * pointer required).  ws: moe_workspace_bytes(MOE_WS_LAYER, ...) bytes; its byte-0 int32
+ * is the error word of moe_pft_build.
+ */
+moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k,
+                               const void *x, const void *wg, const float *bias,
+                               const void *w1, const void *w3, const void *w2, void *out,
+                               const moe_layer_bufs *bufs, void *ws, size_t ws_bytes,
+                               void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

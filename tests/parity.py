@@ -1,0 +1,64 @@
+"""Comparison helpers shared by the parity tests (host side, numpy only)."""
+from __future__ import annotations
+
+import numpy as np
+
+from gemm_gate_softmax_amd import workloads as W
+
+# Tolerances on floating-point layer outputs: max |gpu - oracle| / max |oracle| over the
+# compared tensor (elementwise relative error is ill-posed at the many near-zero outputs).
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+# Near-tie windows on the oracle's double logits: an adjacent gap among a token's k+1
+# largest logits at or below TIE_EXACT * max(1, |l|) may flip the routing under fp32
+# accumulation; the band up to TIE_ACC is counted separately.  Beyond it, a routing
+# mismatch is a failure.
+TIE_EXACT, TIE_ACC = 1e-6, 1e-5
+
+
+def as_f64(a: np.ndarray, dt: str) -> np.ndarray:
+    a = np.asarray(a)
+    return (W.bf16_bits_to_f32(a) if dt == "bf16" else a).astype(np.float64)
+
+
+def max_abs_rel(got, ref, dt) -> float:
+    g, r = as_f64(got, dt), as_f64(ref, dt)
+    if r.size == 0:
+        return 0.0
+    scale = float(np.max(np.abs(r)))
+    return float(np.max(np.abs(g - r))) / (scale if scale > 0 else 1.0)
+
+
+def rms_rel(got, ref, dt) -> float:
+    g, r = as_f64(got, dt), as_f64(ref, dt)
+    den = float(np.sqrt(np.mean(r * r))) or 1.0
+    return float(np.sqrt(np.mean((g - r) ** 2))) / den
+
+
+def tie_bands(l64: np.ndarray, k: int):
+    """Per token: (gap <= TIE_EXACT, TIE_EXACT < gap <= TIE_ACC) over the k+1 largest logits."""
+    T, E = l64.shape
+    m = min(k + 1, E)
+    top = -np.sort(-l64, axis=1)[:, :m]
+    gaps = (top[:, :-1] - top[:, 1:]) / np.maximum(1.0, np.abs(top[:, :-1]))
+    g = gaps.min(axis=1) if m > 1 else np.full(T, np.inf)
+    return g <= TIE_EXACT, (g > TIE_EXACT) & (g <= TIE_ACC)
+
+
+def compare_routing(te_gpu, te_ref, l64, k):
+    """Returns dict(mismatch, tie_exact, tie_acc, bad): tokens whose picks differ, split by
+    near-tie band; `bad` are mismatches outside both bands (must be empty)."""
+    diff = np.any(np.asarray(te_gpu) != np.asarray(te_ref), axis=1)
+    exact, acc = tie_bands(l64, k)
+    return dict(mismatch=np.flatnonzero(diff), tie_exact=np.flatnonzero(diff & exact),
+                tie_acc=np.flatnonzero(diff & acc),
+                bad=np.flatnonzero(diff & ~exact & ~acc))
+
+
+def skewed_routing(rng, T, k, E, alpha=1.0, empty_every=0):
+    """Distinct top-k expert ids per token drawn without replacement from p_e ~ (e+1)^-alpha
+    (Gumbel top-k), optionally never choosing every `empty_every`-th expert."""
+    logp = -alpha * np.log(np.arange(1, E + 1, dtype=np.float64))
+    if empty_every:
+        logp[1::empty_every] = -np.inf
+    keys = logp[None, :] + rng.gumbel(size=(T, E))
+    return np.argsort(-keys, axis=1)[:, :k].astype(np.int32)

@@ -1,0 +1,329 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle on identical inputs.
+
+Routing and buffer indices are compared bit-exactly (routing mismatches are allowed only
+for near-tie tokens, counted and reported); floating-point outputs within the max-abs-
+relative tolerances in ``parity.TOL``.  Inputs are seeded and synthetic.  Every call goes
+through the C ABI via ``gemm_gate_softmax_amd.ops``.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gemm_gate_softmax_amd import ops
+from gemm_gate_softmax_amd import workloads as W
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from parity import (TOL, compare_routing, max_abs_rel, rms_rel, skewed_routing)  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _native():
+    ops.lib()                       # raises if libmoe.so is missing: no fallback exists
+    assert torch.cuda.is_available()
+
+
+def dev(a, dt=None):
+    return W.to_device(a, dt, DEV)
+
+
+def host(t, dt=None):
+    return W.to_host(t, dt)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# --------------------------------------------------------------------------- buffers
+
+PFT_SHAPES = [(0, 2, 8), (1, 1, 1), (5, 3, 7), (256, 2, 8), (1000, 8, 256), (4096, 2, 64),
+              (8192, 6, 64), (4096, 6, 128), (4096, 8, 256), (777, 5, 1000), (3, 64, 64),
+              (1500, 4, 1024)]
+
+
+@pytest.mark.parametrize("T,k,E", PFT_SHAPES)
+def test_pft_parity(orc, T, k, E):
+    rng = np.random.default_rng(T + 7 * k + E)
+    te = skewed_routing(rng, T, k, E, alpha=1.2, empty_every=5 if E >= 5 * k else 0)
+    ref = orc.pft_build(te, E)
+    got = ops.moe_pft_build(dev(te), E)
+    torch.cuda.synchronize()
+    assert int(host(got["ws"][:4].view(torch.int32))[0]) == 0
+    for n in ("counts", "offsets", "token_ids", "expert_ids", "dest_pos"):
+        assert np.array_equal(host(got[n]), ref[n]), n
+
+
+def test_pft_deterministic_and_out_of_range(orc):
+    rng = np.random.default_rng(3)
+    T, k, E = 3000, 8, 256
+    te = skewed_routing(rng, T, k, E)
+    runs = [ops.moe_pft_build(dev(te), E) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for n in ("counts", "offsets", "token_ids", "expert_ids", "dest_pos"):
+            assert torch.equal(r[n], runs[0][n])
+    bad = te.copy()
+    bad[10, 3], bad[2000, 0], bad[2999, 7] = E, -1, 10 ** 6
+    got = ops.moe_pft_build(dev(bad), E)
+    torch.cuda.synchronize()
+    assert int(host(got["ws"][:4].view(torch.int32))[0]) == 3
+    dp = host(got["dest_pos"])
+    assert dp[10, 3] == -1 and dp[2000, 0] == -1 and dp[2999, 7] == -1
+
+
+# ---------------------------------------------------------------- dispatch / combine
+
+MOVE_SHAPES = [(1, 1, 64), (300, 3, 192), (4096, 8, 7168), (513, 6, 2048)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,k,H", MOVE_SHAPES)
+def test_dispatch_parity(orc, dt, T, k, H):
+    rng = np.random.default_rng(T * k + H)
+    x = W._store(rng.standard_normal((T, H)), dt)
+    E = max(2 * k, 16)
+    b = orc.pft_build(skewed_routing(rng, T, k, E), E)
+    ref = orc.dispatch(dt, x, b["dest_pos"])
+    got = ops.moe_dispatch(dev(x, dt), dev(b["dest_pos"]))
+    assert np.array_equal(host(got, dt), ref)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,k,H", MOVE_SHAPES)
+def test_combine_parity(orc, dt, T, k, H):
+    rng = np.random.default_rng(T * k + H + 1)
+    N = T * k
+    y = W._store(rng.standard_normal((N, H)), dt)
+    dpos = rng.permutation(N).astype(np.int32).reshape(T, k)
+    w = rng.random((T, k)).astype(np.float32) + 0.05
+    w /= w.sum(1, keepdims=True)
+    ref = orc.combine(dt, y, dpos, w)
+    got = host(ops.moe_combine(dev(y, dt), dev(dpos), dev(w)), dt)
+    # fp32 FMA chain vs double sum: a few fp32 ulps; bf16: at most one bf16 ulp apart
+    assert max_abs_rel(got, ref, dt) <= (1e-6 if dt == "f32" else 2.0 ** -7)
+    if dt == "bf16":
+        assert np.mean(got != ref) < 0.01
+
+
+# ------------------------------------------------------------------------------ gate
+
+GATE_SHAPES = [(1, 64, 8, 1), (200, 256, 8, 2), (333, 512, 64, 6), (256, 1024, 256, 8),
+               (64, 128, 1000, 8), (130, 192, 6, 6), (64, 64, 64, 64)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,H,E,k", GATE_SHAPES)
+def test_gate_parity(orc, dt, T, H, E, k):
+    cfg = W.LayerConfig("g", T=T, H=H, E=E, F=64, k=k, dtype=dt, bias=("zipf", 1.0))
+    g = W.make_gate_inputs(cfg, seed=T + E)
+    te_ref, tw_ref, _, l64 = orc.gate_topk(dt, g["x"], g["wg"], g["bias"], k, want_logits=True)
+    te, tw = ops.moe_gate_topk(dev(g["x"], dt), dev(g["wg"], dt), dev(g["bias"]), k)
+    te, tw = host(te), host(tw)
+    r = compare_routing(te, te_ref, l64, k)
+    _log(f"gate {dt} T={T} H={H} E={E} k={k}: mismatched={len(r['mismatch'])} "
+         f"(near-tie {len(r['tie_exact'])}, accumulation band {len(r['tie_acc'])})")
+    assert len(r["bad"]) == 0
+    ok = np.setdiff1d(np.arange(T), r["mismatch"])
+    assert np.allclose(tw[ok], tw_ref[ok], rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_gate_exact_logits_bit_exact(orc, dt):
+    # Integer-grid inputs: every partial sum is exact in fp32, so routing must agree with
+    # no exemption at all, ties (broken toward the lower id) included.
+    rng = np.random.default_rng(17)
+    T, H, E, k = 512, 256, 64, 6
+    x = W._store(rng.integers(-2, 3, (T, H)) * 2.0 ** -3, dt)
+    wg = W._store(rng.integers(-2, 3, (E, H)) * 2.0 ** -8, dt)
+    bias = (rng.integers(-4, 5, E) * 2.0 ** -11).astype(np.float32)
+    te_ref, tw_ref = orc.gate_topk(dt, x, wg, bias, k)
+    te, tw = ops.moe_gate_topk(dev(x, dt), dev(wg, dt), dev(bias), k)
+    assert np.array_equal(host(te), te_ref)
+    assert np.allclose(host(tw), tw_ref, rtol=2e-6, atol=1e-7)
+    # all-equal logits: experts 0..k-1 with weight 1/k
+    te, tw = ops.moe_gate_topk(dev(x, dt), torch.zeros_like(dev(wg, dt)), None, k)
+    assert np.array_equal(host(te), np.tile(np.arange(k, dtype=np.int32), (T, 1)))
+    assert np.allclose(host(tw), 1.0 / k, rtol=1e-6)
+
+
+# ------------------------------------------------------------------------ experts
+
+def _segments(rng, E, N, empties=True):
+    """Uneven per-expert row counts summing to N, with empty experts and ragged tails."""
+    w = rng.pareto(1.0, E) + 0.05
+    if empties:
+        w[rng.choice(E, size=max(1, E // 4), replace=False)] = 0.0
+    c = np.floor(w / w.sum() * N).astype(np.int64)
+    c[np.argmax(w)] += N - c.sum()
+    return np.concatenate([[0], np.cumsum(c)]).astype(np.int32)
+
+
+GEMM_SHAPES = [  # (N, E, H, F)
+    (1, 1, 64, 64), (37, 3, 64, 128), (600, 12, 256, 192), (1000, 5, 192, 320),
+    (700, 1, 128, 256), (2000, 40, 128, 128)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,E,H,F", GEMM_SHAPES)
+def test_grouped_gemm_parity(orc, dt, N, E, H, F):
+    rng = np.random.default_rng(N + E + H + F)
+    offsets = _segments(rng, E, N, empties=E > 2)
+    xd = W._store(rng.standard_normal((N, H)), dt)
+    w1 = W._store(rng.standard_normal((E, F, H)) / np.sqrt(H), dt)
+    w3 = W._store(rng.standard_normal((E, F, H)) / np.sqrt(H), dt)
+    w2 = W._store(rng.standard_normal((E, H, F)) / np.sqrt(F), dt)
+    h_ref, y_ref = orc.grouped_gemm_swiglu(dt, xd, offsets, w1, w3, w2)
+    h, y = ops.moe_grouped_gemm_swiglu(dev(xd, dt), dev(offsets), dev(w1, dt), dev(w3, dt),
+                                       dev(w2, dt))
+    h, y = host(h, dt), host(y, dt)
+    eh, ey = max_abs_rel(h, h_ref, dt), max_abs_rel(y, y_ref, dt)
+    _log(f"gemm {dt} N={N} E={E} H={H} F={F}: h err {eh:.2e} y err {ey:.2e} "
+         f"(rms {rms_rel(y, y_ref, dt):.2e})")
+    assert eh <= TOL[dt] and ey <= TOL[dt]
+
+
+# ----------------------------------------------------------------------- whole layer
+
+SMALL_LAYERS = [
+    W.CONFIGS["tiny_f32"],
+    W.LayerConfig("small_bf16", T=300, H=256, E=16, F=192, k=4, dtype="bf16", bias=("zipf", 1.2)),
+    W.LayerConfig("small_f32", T=200, H=128, E=24, F=320, k=6, dtype="f32", bias=("zipf", 1.0)),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL_LAYERS, ids=lambda c: c.name)
+def test_layer_parity_small(orc, cfg):
+    d = W.make_host(cfg, seed=0)
+    dt = cfg.dtype
+    ref = orc.layer_forward(dt, d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k)
+    te_ref, _, _, l64 = orc.gate_topk(dt, d["x"], d["wg"], d["bias"], cfg.k, want_logits=True)
+    out, bufs, ws = ops.moe_layer_forward(dev(d["x"], dt), dev(d["wg"], dt), dev(d["bias"]),
+                                          dev(d["w1"], dt), dev(d["w3"], dt), dev(d["w2"], dt),
+                                          cfg.k)
+    out = host(out, dt)
+    r = compare_routing(host(bufs["top_experts"]), te_ref, l64, cfg.k)
+    assert len(r["bad"]) == 0
+    ok = np.setdiff1d(np.arange(cfg.T), r["mismatch"])
+    err = max_abs_rel(out[ok], ref[ok], dt)
+    _log(f"layer {cfg.name}: err {err:.2e}, near-tie tokens {len(r['mismatch'])}")
+    assert err <= TOL[dt]
+    # buffers of the GPU routing are exactly the oracle's buffers of that routing
+    b_ref = orc.pft_build(host(bufs["top_experts"]), cfg.E)
+    for n in ("counts", "offsets", "token_ids", "expert_ids", "dest_pos"):
+        assert np.array_equal(host(bufs[n]), b_ref[n]), n
+    assert int(host(ws[:4].view(torch.int32))[0]) == 0
+
+
+def test_layer_deterministic():
+    cfg = SMALL_LAYERS[1]
+    d = W.make_device(cfg, seed=1, device=DEV)
+    a = ops.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k)[0]
+    b = ops.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k)[0]
+    assert torch.equal(a, b)
+
+
+def test_layer_zero_tokens():
+    cfg = SMALL_LAYERS[0].scaled(T=0)
+    d = W.make_device(cfg, seed=0, device=DEV)
+    out, _, _ = ops.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k)
+    assert out.shape == (0, cfg.H)
+
+
+def test_rejects_bad_arguments_on_device():
+    x = torch.zeros((8, 64), device=DEV)
+    wg = torch.zeros((4, 64), device=DEV)
+    with pytest.raises(ops.MoeError):
+        ops.moe_gate_topk(x, wg, None, 5)                     # k > E
+    with pytest.raises(ops.MoeError):
+        ops.moe_dispatch(torch.zeros((8, 96), device=DEV), torch.zeros((8, 2), dtype=torch.int32, device=DEV))
+    ws = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ops.MoeError):
+        ops.moe_gate_topk(x, wg, None, 2, ws=ws)              # workspace too small
+
+
+# --------------------------------------------------------- full sizes, sampled outputs
+
+FULL = ["top2_f32", "xmoe_small", "xmoe_medium", "xmoe_large"]
+
+
+def _expert_host(d, e, dt):
+    return tuple(host(d[n][e], dt) for n in ("w1", "w3", "w2"))
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_layer_full_size_sampled(orc, name):
+    cfg = W.CONFIGS[name]
+    dt = cfg.dtype
+    _log(f"[full] {name}: generating inputs")
+    d = W.make_device(cfg, seed=0, device=DEV)
+    out, bufs, ws = ops.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k)
+    torch.cuda.synchronize()
+    assert int(host(ws[:4].view(torch.int32))[0]) == 0
+    x_h, wg_h = host(d["x"], dt), host(d["wg"], dt)
+    bias_h = None if d["bias"] is None else host(d["bias"])
+    # routing of every token
+    _log(f"[full] {name}: oracle gate over all {cfg.T} tokens")
+    te_ref, tw_ref, _, l64 = orc.gate_topk(dt, x_h, wg_h, bias_h, cfg.k, want_logits=True)
+    te, tw = host(bufs["top_experts"]), host(bufs["top_weights"])
+    r = compare_routing(te, te_ref, l64, cfg.k)
+    _log(f"[full] {name}: routing mismatches {len(r['mismatch'])} "
+         f"(near-tie {len(r['tie_exact'])}, accumulation band {len(r['tie_acc'])})")
+    assert len(r["bad"]) == 0
+    ok = np.setdiff1d(np.arange(cfg.T), r["mismatch"])
+    assert np.allclose(tw[ok], tw_ref[ok], rtol=2e-6, atol=1e-7)
+    # buffers: exact, at full size
+    b_ref = orc.pft_build(te, cfg.E)
+    for n in ("counts", "offsets", "token_ids", "expert_ids", "dest_pos"):
+        assert np.array_equal(host(bufs[n]), b_ref[n]), n
+    _log(f"[full] {name}: routing {W.routing_summary(b_ref['counts'])}")
+    # dispatch: every buffer row is its token's row (property, all rows)
+    assert torch.equal(bufs["xd"], d["x"][bufs["token_ids"].long()])
+    # experts: sampled rows, including the first/last rows of the largest and smallest segment
+    counts, offs = b_ref["counts"], b_ref["offsets"]
+    big = int(np.argmax(counts))
+    nz = np.flatnonzero(counts)
+    small = int(nz[np.argmin(counts[nz])])
+    rng = np.random.default_rng(0)
+    rows = {offs[big], offs[big + 1] - 1, (offs[big] + offs[big + 1]) // 2, offs[small],
+            offs[small + 1] - 1, *rng.integers(0, cfg.N, 10).tolist()}
+    rows = sorted(int(p) for p in rows)
+    xd_rows = host(bufs["xd"][rows], dt)
+    h_rows, y_rows = host(bufs["h"][rows], dt), host(bufs["y"][rows], dt)
+    cache = {}
+    for i, p in enumerate(rows):
+        e = int(b_ref["expert_ids"][p])
+        if e not in cache:
+            cache[e] = _expert_host(d, e, dt)
+        w1, w3, w2 = cache[e]
+        h1, y1 = orc.grouped_gemm_swiglu(dt, xd_rows[i:i + 1], np.array([0, 1], np.int32),
+                                         w1[None], w3[None], w2[None])
+        assert max_abs_rel(h_rows[i:i + 1], h1, dt) <= TOL[dt], (p, e)
+        assert max_abs_rel(y_rows[i:i + 1], y1, dt) <= TOL[dt], (p, e)
+    _log(f"[full] {name}: {len(rows)} sampled expert rows match")
+    # combine and the whole chain for sampled tokens, from the oracle's own routing
+    toks = sorted(set(rng.choice(ok, size=min(12, len(ok)), replace=False).tolist()))
+    out_h = host(out, dt)
+    dp = host(bufs["dest_pos"])
+    y_all = bufs["y"]
+    for t in toks:
+        ysub = host(y_all[dp[t].astype(np.int64)], dt)
+        c = orc.combine(dt, ysub, np.arange(cfg.k, dtype=np.int32)[None], tw[t:t + 1])
+        assert max_abs_rel(out_h[t:t + 1], c, dt) <= TOL[dt], t
+        ys = []
+        for j in range(cfg.k):
+            e = int(te_ref[t, j])
+            if e not in cache:
+                cache[e] = _expert_host(d, e, dt)
+            w1, w3, w2 = cache[e]
+            ys.append(orc.grouped_gemm_swiglu(dt, x_h[t:t + 1], np.array([0, 1], np.int32),
+                                              w1[None], w3[None], w2[None], want_h=False)[1])
+        chain = orc.combine(dt, np.concatenate(ys), np.arange(cfg.k, dtype=np.int32)[None],
+                            tw_ref[t:t + 1])
+        assert max_abs_rel(out_h[t:t + 1], chain, dt) <= TOL[dt], t
+    _log(f"[full] {name}: {len(toks)} sampled tokens match end to end")
