@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark: forward pass of one MoE layer on one MI355X, through the C ABI.
+
+One step = one ``moe_layer_forward`` call (gate -> padding-free buffers -> dispatch ->
+grouped SwiGLU experts -> combine) over one batch of synthetic, device-resident input.
+Default workload: the X-MoE Large layer (T=4096, H=7168, E=256, F=2048, top-8, bf16,
+Zipf(1.2) gate bias).  Prints ONE JSON line (see the keys below); with --verbose a
+per-stage table goes to stderr first.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config xmoe_large]
+                  [--no-cpu-baseline] [--cpu-seconds 15]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd tokens/s + grouped-GEMM % MFMA peak, X-MoE Large, 1 GPU"
+HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, published
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="xmoe_large")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--verbose", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, counts):
+    """Algorithmic bytes / flops per stage (what the method itself must move/compute)."""
+    b = 4 if cfg.dtype == "f32" else 2
+    T, H, E, F, k, N = cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, cfg.N
+    active = int((counts > 0).sum())
+    return dict(
+        active_experts=active,
+        gemm_flops=6.0 * N * H * F,
+        gemm_bytes=active * 3.0 * H * F * b + b * (2.0 * N * H + 2.0 * N * F),
+        dispatch_bytes=b * (T * H + N * H) + 4.0 * N,
+        combine_bytes=b * (N * H + T * H) + 8.0 * N,
+        gate_bytes=b * (T * H + E * H) + 8.0 * T * k,
+        gate_flops=2.0 * T * E * H,
+    )
+
+
+def time_calls(fn, iters, stream):
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters        # ms per call
+
+
+def cpu_baseline(cfg, d, seed, target_s):
+    """The oracle, as it is, on the first tokens of the same workload (bounded sample)."""
+    import numpy as np
+
+    import oracle
+    from gemm_gate_softmax_amd import workloads as W
+
+    dt = cfg.dtype
+    x_all, wg = W.to_host(d["x"], dt), W.to_host(d["wg"], dt)
+    bias = None if d["bias"] is None else W.to_host(d["bias"], None)
+    w_host = {n: np.empty(tuple(d[n].shape), np.float32 if dt == "f32" else np.uint16)
+              for n in ("w1", "w3", "w2")}      # pages of unused experts are never touched
+    loaded = set()
+
+    def run(ntok):
+        te, _ = oracle.gate_topk(dt, x_all[:ntok], wg, bias, cfg.k)
+        for e in sorted(set(te.reshape(-1).tolist()) - loaded):
+            for n in ("w1", "w3", "w2"):
+                w_host[n][e] = W.to_host(d[n][e], dt)
+            loaded.add(e)
+        t0 = time.perf_counter()
+        _, secs = oracle.layer_forward(dt, x_all[:ntok], wg, bias, w_host["w1"], w_host["w3"],
+                                       w_host["w2"], cfg.k, stage_seconds=True)
+        return time.perf_counter() - t0, secs
+
+    probe = 8
+    t_probe, _ = run(probe)
+    ntok = int(min(cfg.T, max(probe, probe * target_s / max(t_probe, 1e-3))))
+    wall, secs = run(ntok)
+    return {"value": ntok / wall, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {ntok} of {cfg.T} tokens of the same {cfg.name} layer (same weights), "
+                      f"oracle_layer_forward end to end, {wall:.1f} s; stage seconds gate/buffers/"
+                      f"dispatch/experts/combine = {', '.join(f'{s:.2f}' for s in secs)}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        log("bench.py: only --gpus 1 is supported (single-GPU layer forward)")
+        return 2
+
+    import numpy as np
+    import torch
+
+    from gemm_gate_softmax_amd import ops
+    from gemm_gate_softmax_amd import workloads as W
+
+    cfg = W.CONFIGS[args.config]
+    dev = "cuda"
+    ops.lib()                                   # the HIP library or nothing
+    log(f"bench: {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} F={cfg.F} k={cfg.k} {cfg.dtype}: "
+        "drawing inputs on the device")
+    d = W.make_device(cfg, seed=args.seed, device=dev)
+    bufs = ops.alloc_layer_bufs(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, d["x"].dtype, dev)
+    dtc = ops.dtype_code(d["x"].dtype)
+    ws = ops.workspace(ops.MOE_WS_LAYER, cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, dtc, dev)
+    out = torch.empty_like(d["x"])
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ops.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k,
+                              out=out, bufs=bufs, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    counts = W.to_host(bufs["counts"], None)
+    log(f"bench: routing {W.routing_summary(counts)}; timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_events = time_calls(step, args.steps, stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # Per-stage times: each entry point on its own, same buffers, same stream.
+    N = cfg.N
+    gws = ops.workspace(ops.MOE_WS_GEMM, N, cfg.H, cfg.E, cfg.F, 1, dtc, dev)
+    pws = ops.workspace(ops.MOE_WS_PFT, cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, dtc, dev)
+    gtw = ops.workspace(ops.MOE_WS_GATE, cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, dtc, dev)
+    pft_out = {n: bufs[n] for n in ("counts", "offsets", "token_ids", "expert_ids", "dest_pos")}
+    stages = {
+        "gate": lambda: ops.moe_gate_topk(d["x"], d["wg"], d["bias"], cfg.k, bufs["top_experts"],
+                                          bufs["top_weights"], ws=gtw),
+        "buffers": lambda: ops.moe_pft_build(bufs["top_experts"], cfg.E, out=pft_out, ws=pws),
+        "dispatch": lambda: ops.moe_dispatch(d["x"], bufs["dest_pos"], xd=bufs["xd"]),
+        "grouped_gemm": lambda: ops.moe_grouped_gemm_swiglu(bufs["xd"], bufs["offsets"], d["w1"],
+                                                            d["w3"], d["w2"], h=bufs["h"],
+                                                            y=bufs["y"], ws=gws),
+        "combine": lambda: ops.moe_combine(bufs["y"], bufs["dest_pos"], bufs["top_weights"],
+                                           out=out),
+    }
+    st_ms = {}
+    for name, fn in stages.items():
+        fn()
+        torch.cuda.synchronize()
+        st_ms[name] = time_calls(fn, args.steps, stream)
+    alg = algorithmic(cfg, counts)
+    g_ms = st_ms["grouped_gemm"]
+    tflops = alg["gemm_flops"] / (g_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    stage_report = {n: round(v * 1e3, 2) for n, v in st_ms.items()}
+    bw = {
+        "dispatch_GBs": alg["dispatch_bytes"] / (st_ms["dispatch"] * 1e-3) / 1e9,
+        "combine_GBs": alg["combine_bytes"] / (st_ms["combine"] * 1e-3) / 1e9,
+        "grouped_gemm_GBs": alg["gemm_bytes"] / (g_ms * 1e-3) / 1e9,
+    }
+    if args.verbose:
+        for n, v in st_ms.items():
+            log(f"  {n:13s} {v * 1e3:9.1f} us")
+        log(f"  grouped GEMM {tflops:.1f} TFLOP/s = {100 * tflops / peak:.1f}% of {peak} "
+            f"(weights+activations {bw['grouped_gemm_GBs']:.0f} GB/s); dispatch "
+            f"{bw['dispatch_GBs']:.0f} GB/s, combine {bw['combine_GBs']:.0f} GB/s")
+
+    rec = {
+        "metric": METRIC, "value": cfg.T / (ms_events * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_events, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "F": cfg.F,
+                   "k": cfg.k, "gate_bias": None if cfg.bias is None else f"{cfg.bias[0]}({cfg.bias[1]})",
+                   "seed": args.seed, "active_experts": alg["active_experts"],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None,
+                     "kernel": "moe_grouped_gemm_swiglu (tile table + gate/up SwiGLU + down)"},
+        "stages_us": stage_report,
+        "bandwidth": {k_: round(v, 1) for k_, v in bw.items()}
+        | {"dispatch_frac_hbm": round(bw["dispatch_GBs"] / HBM_PEAK_GBS, 4),
+           "combine_frac_hbm": round(bw["combine_GBs"] / HBM_PEAK_GBS, 4),
+           "grouped_gemm_frac_hbm": round(bw["grouped_gemm_GBs"] / HBM_PEAK_GBS, 4)},
+        "wall_ms_per_step": wall_ms,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline(cfg, d, args.seed, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

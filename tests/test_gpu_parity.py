@@ -16,7 +16,8 @@ from gemm_gate_softmax_amd import ops
 from gemm_gate_softmax_amd import workloads as W
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-from parity import (TOL, compare_routing, max_abs_rel, rms_rel, skewed_routing)  # noqa: E402
+from parity import (TOL, WEIGHT_ATOL, compare_routing, max_abs_rel, rms_rel,  # noqa: E402
+                    skewed_routing)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -130,7 +131,9 @@ def test_gate_parity(orc, dt, T, H, E, k):
          f"(near-tie {len(r['tie_exact'])}, accumulation band {len(r['tie_acc'])})")
     assert len(r["bad"]) == 0
     ok = np.setdiff1d(np.arange(T), r["mismatch"])
-    assert np.allclose(tw[ok], tw_ref[ok], rtol=2e-6, atol=1e-7)
+    dw = float(np.max(np.abs(tw[ok] - tw_ref[ok]))) if len(ok) else 0.0
+    _log(f"    max |dw| {dw:.2e}")
+    assert dw <= WEIGHT_ATOL
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -145,7 +148,8 @@ def test_gate_exact_logits_bit_exact(orc, dt):
     te_ref, tw_ref = orc.gate_topk(dt, x, wg, bias, k)
     te, tw = ops.moe_gate_topk(dev(x, dt), dev(wg, dt), dev(bias), k)
     assert np.array_equal(host(te), te_ref)
-    assert np.allclose(host(tw), tw_ref, rtol=2e-6, atol=1e-7)
+    # exact logits: only exp and the division round, a few fp32 ulps
+    assert np.allclose(host(tw), tw_ref, rtol=1e-6, atol=1e-7)
     # all-equal logits: experts 0..k-1 with weight 1/k
     te, tw = ops.moe_gate_topk(dev(x, dt), torch.zeros_like(dev(wg, dt)), None, k)
     assert np.array_equal(host(te), np.tile(np.arange(k, dtype=np.int32), (T, 1)))
@@ -276,7 +280,7 @@ def test_layer_full_size_sampled(orc, name):
          f"(near-tie {len(r['tie_exact'])}, accumulation band {len(r['tie_acc'])})")
     assert len(r["bad"]) == 0
     ok = np.setdiff1d(np.arange(cfg.T), r["mismatch"])
-    assert np.allclose(tw[ok], tw_ref[ok], rtol=2e-6, atol=1e-7)
+    assert np.max(np.abs(tw[ok] - tw_ref[ok])) <= WEIGHT_ATOL
     # buffers: exact, at full size
     b_ref = orc.pft_build(te, cfg.E)
     for n in ("counts", "offsets", "token_ids", "expert_ids", "dest_pos"):
