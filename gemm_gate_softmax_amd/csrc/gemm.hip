@@ -18,10 +18,10 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBTok = 128;      // activation rows per tile
-constexpr int kBFeat = 128;     // weight rows (output features) per tile and operand
-constexpr int kStageBytes = 128;  // bytes of K per row staged per main-loop step
-constexpr int kLdsStride = 144;   // padded LDS row pitch: conflict-free 16-byte reads
+constexpr int kBTok = 128;        // activation rows per tile
+constexpr int kBFeat = 128;       // weight rows (output features) per tile and operand
+constexpr int kRowBytes = 128;    // bytes of K per row and stage (64 bf16 or 32 fp32)
+constexpr int kStages = 3;        // LDS ring depth: two stages in flight while one is used
 
 enum Epilogue { kEpiLogits = 0, kEpiSwiGLU = 1, kEpiStore = 2 };
 
@@ -43,12 +43,43 @@ struct GemmParams {
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
+// One 16-byte global -> LDS transfer per lane, no register round trip (gfx950).  The LDS
+// destination of a wave's instruction is the 1 KiB block at byte address `lds_block`
+// (wave-uniform, passed in M0), lane L landing at byte 16 L; the global source is per
+// lane.  Issued from inline asm so that the compiler's wait insertion does not treat the
+// transfer as a pending write of every LDS address (that would drain the whole ring before
+// each LDS read); the ring's waits are explicit (wait_vm_and_barrier).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_block) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "{m0}"(lds_block)
+                 : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding, then meet
+// the other waves.  Written as one asm statement with a memory clobber so the compiler
+// neither moves LDS accesses across it nor adds a full drain of the in-flight stages.
+template <int N>
+__device__ __forceinline__ void wait_vm_and_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // simm16: vmcnt[3:0] | expcnt[6:4] (7 = no wait) | lgkmcnt[11:8] (15 = no wait) | vmcnt[5:4] << 14
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+}
+
+// LDS tile layout: each stage holds kBTok activation rows then NB*kBFeat weight rows, 128
+// bytes each, unpadded.  The 16-byte chunk c of row r sits in slot c ^ swz(r) with
+// swz(r) = (r & 7) ^ ((r >> 3) & 1): 16 lanes reading rows r0..r0+15 (r0 % 16 == 0) at
+// one k-chunk then touch 16 distinct 16-byte bank groups of a 256-byte line, and any 8
+// of them 8 distinct groups of a 128-byte line.
 template <typename T, int NB, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(GemmParams<T, NB> p) {
-    constexpr int kRows = kBTok + NB * kBFeat;            // LDS rows per stage
-    constexpr int kAChunks = kBTok * 8 / kThreads;        // 16-byte loads per thread (A)
-    constexpr int kBChunks = NB * kBFeat * 8 / kThreads;  // (B)
-    __shared__ __attribute__((aligned(16))) char lds[2][kRows * kLdsStride];
+    constexpr int kRows = kBTok + NB * kBFeat;       // LDS rows per stage
+    constexpr int kStageBytes = kRows * kRowBytes;
+    constexpr int kBlocks = kRows / 8;               // 1 KiB blocks per stage
+    constexpr int kDma = kBlocks / 4;                // DMA instructions per wave per stage
+    static_assert(kBlocks % 4 == 0 && kBTok % 32 == 0 && kBFeat % 32 == 0, "tile shape");
+    __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
 
     // ---- which tile: XCD-contiguous order over (expert, feature tile, token tile) ----
     const int ntt = p.table ? *p.table_count : (p.dense_rows + kBTok - 1) / kBTok;
@@ -70,30 +101,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(GemmParams<T, NB> 
     const int row_end = min(seg0 + segn, p.act_rows);
     const int f0 = ftile * kBFeat;
 
-    // ---- per-thread global source rows (clamped into valid memory) ----
     const int tid = threadIdx.x;
-    const int lrow = tid >> 3, lch = tid & 7;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const size_t row_bytes = (size_t)p.K * sizeof(T);
-    const char* a_src[kAChunks];
-    const char* b_src[kBChunks];
+
+    // ---- DMA sources: wave w fills blocks w + 4 i of every stage (8 rows per block) ----
+    // Block b < kBTok/8 holds activation rows, the rest weight rows of operand
+    // (b*8 - kBTok) / kBFeat: both are compile-time once i is unrolled (w < 4).
+    const char* src[kDma];
 #pragma unroll
-    for (int i = 0; i < kAChunks; ++i) {
-        const int r = min(row0 + lrow + 32 * i, p.act_rows - 1);
-        a_src[i] = reinterpret_cast<const char*>(p.act) + (size_t)r * row_bytes + lch * 16;
+    for (int i = 0; i < kDma; ++i) {
+        const int r = (wave + 4 * i) * 8 + (lane >> 3);            // row within the stage
+        const int c = (lane & 7) ^ (lane >> 3) ^ (wave & 1);        // chunk held by slot lane&7
+        if (i < kBTok / 32) {
+            const int ar = min(row0 + r, p.act_rows - 1);
+            src[i] = reinterpret_cast<const char*>(p.act) + (size_t)ar * row_bytes + c * 16;
+        } else {
+            constexpr int kB0 = kBTok / 32;
+            const int b = (i - kB0) / (kBFeat / 32);
+            const int f = min(f0 + (r - kBTok) % kBFeat, p.n_feat - 1);
+            src[i] = reinterpret_cast<const char*>(p.w[b] + (size_t)expert * p.w_stride) +
+                     (size_t)f * row_bytes + c * 16;
+        }
     }
+    const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) char*)(lds)));
+    auto issue = [&](int kt, int slot) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base + slot * kStageBytes + wave * 1024);
+        const size_t off = (size_t)kt * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i) {
-        // lrow < 32 and kBFeat is a multiple of 32, so the operand index is (32 i) / kBFeat:
-        // a constant once the loop is unrolled (no dynamic indexing of the argument array).
-        const int b = (32 * i) / kBFeat;
-        const int f = min(f0 + lrow + (32 * i) % kBFeat, p.n_feat - 1);
-        b_src[i] = reinterpret_cast<const char*>(p.w[b] + (size_t)expert * p.w_stride) +
-                   (size_t)f * row_bytes + lch * 16;
-    }
+        for (int i = 0; i < kDma; ++i) dma16(src[i] + off, base + i * 4096);
+    };
+
     // ---- wave layout: 2 x 2 waves, each 64 token rows x 64 features per operand ----
-    const int wave = tid >> 6, lane = tid & 63;
     const int wt = wave & 1, wf = wave >> 1;
     const int l16 = lane & 15, lgrp = lane >> 4;
+    const int swz = (l16 & 7) ^ (l16 >> 3);
     f32x4_t acc[NB][4][4];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -102,43 +146,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(GemmParams<T, NB> 
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[b][i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Stage loads land in registers first (ra, rb) and are written to the other LDS
-    // buffer after this step's MFMAs, so global latency hides behind the math.
-    uint4 ra[kAChunks], rb[kBChunks];
-    const int nk = (int)(row_bytes / kStageBytes);
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i]);
-#pragma unroll
-    for (int i = 0; i < kBChunks; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i]);
-#pragma unroll
-    for (int i = 0; i < kAChunks; ++i)
-        *reinterpret_cast<uint4*>(&lds[0][(lrow + 32 * i) * kLdsStride + lch * 16]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < kBChunks; ++i)
-        *reinterpret_cast<uint4*>(&lds[0][(kBTok + lrow + 32 * i) * kLdsStride + lch * 16]) = rb[i];
-    __syncthreads();
+    const int nk = (int)(row_bytes / kRowBytes);
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    int slot = 0;
     for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < nk;
-        const size_t off = (size_t)(more ? kt + 1 : kt) * kStageBytes;
+        // stage kt landed (only stage kt+1 may still be in flight) and every wave is done
+        // reading the slot that stage kt+2 is about to overwrite
+        if (kt + 1 < nk) wait_vm_and_barrier<kDma>();
+        else wait_vm_and_barrier<0>();
+        if (kt + 2 < nk) issue(kt + 2, slot == 0 ? 2 : slot - 1);
+        const char* st = lds + slot * kStageBytes;
 #pragma unroll
-        for (int i = 0; i < kAChunks; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + off);
-#pragma unroll
-        for (int i = 0; i < kBChunks; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + off);
-#pragma unroll
-        for (int kg = 0; kg < kStageBytes / 64; ++kg) {
-            const int col = kg * 64 + lgrp * 16;
+        for (int kg = 0; kg < kRowBytes / 64; ++kg) {
+            const int cs = ((kg * 4 + lgrp) ^ swz) * 16;
             uint4 fa[4], fw[NB][4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                fa[i] = *reinterpret_cast<const uint4*>(
-                    &lds[buf][(wt * 64 + i * 16 + l16) * kLdsStride + col]);
+                fa[i] = *reinterpret_cast<const uint4*>(st + (wt * 64 + i * 16 + l16) * kRowBytes + cs);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     fw[b][i] = *reinterpret_cast<const uint4*>(
-                        &lds[buf][(kBTok + b * kBFeat + wf * 64 + i * 16 + l16) * kLdsStride + col]);
+                        st + (kBTok + b * kBFeat + wf * 64 + i * 16 + l16) * kRowBytes + cs);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -146,15 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(GemmParams<T, NB> 
 #pragma unroll
                     for (int j = 0; j < 4; ++j) Mfma<T>::mac(acc[b][i][j], fw[b][i], fa[j]);
         }
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < kAChunks; ++i)
-                *reinterpret_cast<uint4*>(&lds[buf ^ 1][(lrow + 32 * i) * kLdsStride + lch * 16]) = ra[i];
-#pragma unroll
-            for (int i = 0; i < kBChunks; ++i)
-                *reinterpret_cast<uint4*>(&lds[buf ^ 1][(kBTok + lrow + 32 * i) * kLdsStride + lch * 16]) = rb[i];
-        }
-        __syncthreads();
+        slot = slot == kStages - 1 ? 0 : slot + 1;
     }
 
     // ---- epilogue: lane holds token (l16) x 4 consecutive features ----
