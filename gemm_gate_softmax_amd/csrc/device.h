@@ -116,27 +116,31 @@ __device__ __forceinline__ uint32_t f32_order_key(float f) {
 }
 
 // ------------------------------------------------------------------------ MFMA --
-// Both steps consume one 16-byte chunk per lane from each operand ("a k-group") and
-// accumulate a 16x16 fp32 tile.  Lane l supplies row (l % 16) of the A side and
-// column (l % 16) of the B side; its k-group slice is chunk (l / 16) of the 64-byte
-// k-group.  The result tile holds column (l % 16), rows 4*(l/16) + v, v = 0..3.
+// 32x32 output tiles: on gfx950 the 32x32x16 bf16 instruction sustains about 2.1-2.2
+// PFLOP/s chip-wide against about 1.3 for 16x16x32, so every product uses 32x32 tiles.
+// One "k-step" consumes one 16-byte chunk per lane from each operand: lane l supplies
+// row (l % 32) of the A side and column (l % 32) of the B side, and its chunk holds the
+// k-slice of half l / 32 of the step.  The result tile gives lane l column (l % 32) and
+// rows 8 j + 4 (l / 32) + v in register 4 j + v (j, v = 0..3).
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
 template <typename T> struct Mfma;
 
 template <> struct Mfma<bf16_t> {
-    static constexpr int kElemsPerKGroup = 32;  // 16x16x32: one instruction per k-group
-    __device__ static __forceinline__ void mac(f32x4_t& c, const uint4& a, const uint4& b) {
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+    // one 32x32x16 instruction: the chunk is 8 consecutive k of this lane's half
+    __device__ static __forceinline__ void mac(f32x16_t& c, const uint4& a, const uint4& b) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                     __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     }
 };
 
 template <> struct Mfma<float> {
-    static constexpr int kElemsPerKGroup = 16;  // 4 x 16x16x4: element s of each lane's chunk
-    __device__ static __forceinline__ void mac(f32x4_t& c, const uint4& a, const uint4& b) {
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    // four 32x32x2 instructions: element e of the chunk is this lane's k for the e-th one
+    __device__ static __forceinline__ void mac(f32x16_t& c, const uint4& a, const uint4& b) {
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
     }
 };
 
