@@ -8,9 +8,13 @@
 // contributes no tile, so its weights are never read.
 //
 // Every product here is "NT": both operands are rows contiguous in the shared dimension
-// K (activations [rows][K], weights [features][K]).  One workgroup (4 waves) computes a
-// tile of kBTok activation rows x kBFeat weight rows for NB weight operands at once (NB = 2
-// fuses the SwiGLU gate and up products so the epilogue can form silu(a) * g in registers).
+// K (activations [rows][K], weights [features][K]).  NB = 2 fuses the SwiGLU gate and up
+// products so the epilogue forms silu(a) * g in registers.
+//
+// Every tile is 128 tokens x (128 x NB or 256) features, its operands staged through an
+// LDS ring by direct-to-LDS transfers and consumed by 4 waves in a 2 x 2 layout.  An
+// expert with a handful of rows still gets a whole tile: its time goes to streaming the
+// expert's weights, which measured no slower through this path than through registers.
 #include "device.h"
 #include "launch.h"
 
@@ -21,21 +25,15 @@ constexpr int kThreads = 256;
 
 enum Epilogue { kEpiLogits = 0, kEpiSwiGLU = 1, kEpiStore = 2 };
 
-// Tile shapes.  Expert products: 256 token rows x 128 features x 2 operands (gate/up with
-// SwiGLU) or 256 x 256 x 1 (down); both use 512 LDS rows per stage (32 KiB) and a
-// 5-stage ring, so 4 stages (128 KiB) are in flight while one is consumed.  The gate
-// logits use small 64 x 64 tiles so a few thousand tokens still fill the chip.
-#ifndef MOE_EXPERT_BTOK
-#define MOE_EXPERT_BTOK 128
-#define MOE_EXPERT_UP_BF 128
-#define MOE_EXPERT_DOWN_BF 256
-#define MOE_EXPERT_STAGES 3
-#endif
-constexpr int kExpertBTok = MOE_EXPERT_BTOK;
-constexpr int kExpertUpBF = MOE_EXPERT_UP_BF;
-constexpr int kExpertDownBF = MOE_EXPERT_DOWN_BF;
-constexpr int kExpertStages = MOE_EXPERT_STAGES;
-constexpr int kGroupTok = 4;      // token tiles per L2-sharing block (see gemm_nt_kernel)
+// Tile shapes.  Expert products: 128 tokens; up product 128 features x 2 operands, down
+// product 256 features; a 3-slot ring of 48 KiB k-slices (64 k per row, whole 128-byte
+// lines).  The gate logits use small 64 x 64 tiles so a few thousand tokens still fill
+// the chip.
+constexpr int kExpertBTok = 128;
+constexpr int kExpertUpBF = 128;
+constexpr int kExpertDownBF = 256;
+constexpr int kExpertStages = 3;
+constexpr int kGroupTok = 4;      // token tiles per L2-sharing block (see expert_tile_of)
 
 template <typename T, int NB>
 struct GemmParams {
@@ -45,13 +43,36 @@ struct GemmParams {
     const T* w[NB];         // weight operands; expert e starts at w[b] + e * w_stride
     long long w_stride;     // elements per expert
     int n_feat;             // output features (weight rows per expert)
-    int feat_tiles;         // ceil(n_feat / BF)
-    const int4* table;      // per token tile: (expert, first tile of expert, row0, rows); null = dense
-    const int* table_count; // number of token tiles in table
-    int dense_rows;         // rows when table is null (single expert 0)
+    int feat_tiles;         // compute tiles per token tile: ceil(n_feat / BF)
+    const int4* table;      // compute token tiles: (expert, first tile of expert, row0, rows)
+    const int* table_count; // entries in table
+    int dense_rows;         // rows of the single expert of a dense product (gate)
     void* out;              // [rows][n_feat]: fp32 logits or storage type
     const float* bias;      // logits epilogue only (nullable)
 };
+
+// Writes 4 consecutive features of one token: fp32 logits (+ bias, per-element bounds),
+// or the storage type (n_feat is a multiple of 64, so a run never straddles the end).
+template <typename T, int NB, int EPI>
+__device__ __forceinline__ void store_run(const GemmParams<T, NB>& p, int tok, int feat,
+                                          const float (&r)[4]) {
+    if constexpr (EPI == kEpiLogits) {
+        float* o = reinterpret_cast<float*>(p.out) + (size_t)tok * p.n_feat;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            if (feat + v < p.n_feat) o[feat + v] = r[v] + (p.bias ? p.bias[feat + v] : 0.0f);
+    } else if constexpr (sizeof(T) == 4) {
+        if (feat >= p.n_feat) return;
+        float* o = reinterpret_cast<float*>(p.out) + (size_t)tok * p.n_feat + feat;
+        *reinterpret_cast<float4*>(o) = make_float4(r[0], r[1], r[2], r[3]);
+    } else {
+        if (feat >= p.n_feat) return;
+        uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (size_t)tok * p.n_feat + feat;
+        const uint32_t lo = f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
+        const uint32_t hi = f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
+        *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+    }
+}
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
@@ -94,50 +115,30 @@ __device__ __forceinline__ void wait_stages(int m) {
 // half-line requests measured ~30% slower at the L2), unpadded.  The 16-byte chunk c of
 // row r sits in slot c ^ (r & 7), which reads as fast as fully contiguous data for the
 // 32x32 fragment pattern (lane l: row r0 + l % 32, chunk c0 + l / 32).
+template <int BT, int BF, int NB, int S>
+struct CompTile {
+    static constexpr int kRowBytes = 128;                   // bytes of K per row and stage
+    static constexpr int kRows = BT + NB * BF;              // LDS rows per stage
+    static constexpr int kStageBytes = kRows * kRowBytes;
+    static constexpr int kLdsBytes = S * kStageBytes;
+};
+
+// One compute tile: activation rows [row0, row0 + BT) (stored below row_end) against
+// weight rows [f0, f0 + BF) of each operand of `expert`.
 template <typename T, int NB, int EPI, int BT, int BF, int S>
-__global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(GemmParams<T, NB> p) {
-    constexpr int kRowBytes = 128;                   // bytes of K per row and stage
+__device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* lds, int expert,
+                                             int row0, int row_end, int f0) {
+    constexpr int kRowBytes = CompTile<BT, BF, NB, S>::kRowBytes;
     constexpr int kRowsPerDma = 1024 / kRowBytes;    // rows per 1 KiB DMA instruction
     constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
-    constexpr int kRows = BT + NB * BF;              // LDS rows per stage
-    constexpr int kStageBytes = kRows * kRowBytes;
+    constexpr int kRows = CompTile<BT, BF, NB, S>::kRows;
+    constexpr int kStageBytes = CompTile<BT, BF, NB, S>::kStageBytes;
     constexpr int kDma = kRows / (4 * kRowsPerDma);  // DMA instructions per wave per stage
     constexpr int TT = BT / 64, FT = BF / 64;        // 32x32 tiles per wave (tokens, features)
     constexpr int KS = kRowBytes / 32;               // k-steps (16-byte chunk pairs) per stage
     static_assert(kRows % (4 * kRowsPerDma) == 0 && BT % 64 == 0 && BF % 64 == 0, "tile shape");
     static_assert(BT % (4 * kRowsPerDma) == 0 && BF % (4 * kRowsPerDma) == 0, "operand blocks");
     static_assert(S >= 2 && (S - 2) * kDma < 64 && S * kStageBytes <= 160 * 1024, "ring");
-    __shared__ __attribute__((aligned(1024))) char lds[S * kStageBytes];
-
-    // ---- which tile: XCD-contiguous order over (expert, feature tile, token tile) ----
-    const int ntt = p.table ? *p.table_count : (p.dense_rows + BT - 1) / BT;
-    const int total = ntt * p.feat_tiles;
-    const int chunk = (total + 7) >> 3;
-    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    if (local >= chunk) return;
-    const int L = xcd * chunk + local;
-    if (L >= total) return;
-    int expert = 0, first = 0, seg0 = 0, segn = p.dense_rows;
-    if (p.table) {
-        const int4 te = p.table[L / p.feat_tiles];
-        expert = te.x; first = te.y; seg0 = te.z; segn = te.w;
-    }
-    // Within an expert, tiles go in blocks of kGroupTok token tiles; inside a block the
-    // feature tile varies slowest.  The 32 tiles an XCD runs at once then cover about
-    // 4 token tiles x 8 feature tiles, so both operands are shared through that XCD's L2
-    // (a single token-tile column would share the weights but re-read every activation
-    // panel).  Experts with one token tile reduce to feature-tile order.
-    const int n_e = (segn + BT - 1) / BT;
-    const int q = L - p.feat_tiles * first;
-    const int blk_tiles = kGroupTok * p.feat_tiles;
-    const int blk = min(q / blk_tiles, (n_e - 1) / kGroupTok);
-    const int width = min(kGroupTok, n_e - blk * kGroupTok);
-    const int ql = q - blk * blk_tiles;
-    const int ftile = ql / width;
-    const int ttile = blk * kGroupTok + (ql - ftile * width);
-    const int row0 = seg0 + ttile * BT;
-    const int row_end = min(seg0 + segn, p.act_rows);
-    const int f0 = ftile * BF;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -166,12 +167,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(GemmParams<T, NB> 
     }
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
         (__attribute__((address_space(3))) char*)(lds)));
-    auto issue = [&](int kt, int slot) {
-        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base + slot * kStageBytes + wave * 1024);
-        const size_t off = (size_t)kt * kRowBytes;
-#pragma unroll
-        for (int i = 0; i < kDma; ++i) dma16(src[i] + off, base + i * 4096);   // 4 waves x 1 KiB
-    };
+    // DMA instructions [i0, i0 + n) of stage kt into LDS slot `slot` (i0 and n are
+    // compile-time after unrolling).
+#define MOE_ISSUE(KT, SLOT, I0, NI)                                                           \
+    do {                                                                                     \
+        const uint32_t base_ = __builtin_amdgcn_readfirstlane(lds_base + (SLOT) * kStageBytes + wave * 1024); \
+        const size_t off_ = (size_t)(KT) * kRowBytes;                                        \
+        _Pragma("unroll") for (int i_ = (I0); i_ < (I0) + (NI); ++i_)                        \
+            dma16(src[i_] + off_, base_ + i_ * 4096);   /* 4 waves x 1 KiB */                \
+    } while (0)
 
     // ---- wave layout: 2 x 2 waves, each (BT/2) tokens x (BF/2) features per operand,
     // as TT x FT tiles of 32 x 32 (MFMA rows = features, MFMA columns = tokens) ----
@@ -213,28 +217,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(GemmParams<T, NB> 
     } while (0)
     static_assert(KS % 2 == 0, "k-steps alternate between the two fragment buffers");
 
+    // DMA for stage kt+S-1 is spread over the KS k-steps of stage kt (a quarter per
+    // k-step) into the slot stage kt-1 vacated, so requests leave each wave steadily
+    // rather than in one burst at the barrier.
+    static_assert(kDma % KS == 0, "DMA instructions split evenly over the k-steps");
+    constexpr int kPart = kDma / KS;
     const int nk = (int)(row_bytes / kRowBytes);
-    for (int s = 0; s < S && s < nk; ++s) issue(s, s);
-    wait_stages<kDma, S - 1, false>(min(S - 1, nk - 1));          // stage 0 landed
+    for (int s = 0; s < S - 1 && s < nk; ++s) MOE_ISSUE(s, s, 0, kDma);
+    wait_stages<kDma, S - 2, false>(min(S - 2, nk - 1));          // stage 0 landed
     MOE_LOAD_FRAGS(lds, 0, fa0, fw0);
     // The last stage is peeled off so every loop iteration has the same shape (otherwise
     // the compiler's wait insertion merges paths and drains the prefetched fragments).
-    int slot = 0;
+    int slot = 0, refill = S - 1;
     for (int kt = 0; kt < nk - 1; ++kt) {
         const char* st = lds + slot * kStageBytes;
         const int next = slot == S - 1 ? 0 : slot + 1;
+        const bool more = kt + S - 1 < nk;
 #pragma unroll
         for (int ks = 0; ks < KS; ks += 2) {
             MOE_LOAD_FRAGS(st, ks + 1, fa1, fw1);
+            if (more) MOE_ISSUE(kt + S - 1, refill, ks * kPart, kPart);
             __builtin_amdgcn_sched_barrier(0);
             MOE_MFMAS(fa0, fw0);
             __builtin_amdgcn_sched_barrier(0);
+            if (more) MOE_ISSUE(kt + S - 1, refill, (ks + 1) * kPart, kPart);
             if (ks + 2 < KS) {
                 MOE_LOAD_FRAGS(st, ks + 2, fa0, fw0);
             } else {
                 // this wave's reads of stage kt are complete; stage kt+1 landed everywhere
                 wait_stages<kDma, (S >= 2 ? S - 2 : 0), true>(min(S - 2, nk - 2 - kt));
-                if (kt + S < nk) issue(kt + S, slot);
                 MOE_LOAD_FRAGS(lds + next * kStageBytes, 0, fa0, fw0);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -242,6 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(GemmParams<T, NB> 
             __builtin_amdgcn_sched_barrier(0);
         }
         slot = next;
+        refill = refill == S - 1 ? 0 : refill + 1;
     }
     {
         const char* st = lds + slot * kStageBytes;
@@ -255,6 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(GemmParams<T, NB> 
     }
 #undef MOE_LOAD_FRAGS
 #undef MOE_MFMAS
+#undef MOE_ISSUE
 
     // ---- epilogue: lane holds one token and, per 32-feature tile, 4 runs of 4 features ----
 #pragma unroll
@@ -266,55 +279,81 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(GemmParams<T, NB> 
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int feat = f0 + wf * (BF / 2) + i * 32 + 8 * g + 4 * lhalf;
-                float a[4];
+                float r[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) a[v] = acc[0][i][j][4 * g + v];
-                if constexpr (EPI == kEpiLogits) {
-                    float* o = reinterpret_cast<float*>(p.out) + (size_t)tok * p.n_feat;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (feat + v < p.n_feat) o[feat + v] = a[v] + (p.bias ? p.bias[feat + v] : 0.0f);
-                } else {
-                    if (feat >= p.n_feat) continue;
-                    float r[4];
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        if constexpr (EPI == kEpiSwiGLU) r[v] = silu(a[v]) * acc[NB - 1][i][j][4 * g + v];
-                        else r[v] = a[v];
-                    }
-                    if constexpr (sizeof(T) == 4) {
-                        float* o = reinterpret_cast<float*>(p.out) + (size_t)tok * p.n_feat + feat;
-                        *reinterpret_cast<float4*>(o) = make_float4(r[0], r[1], r[2], r[3]);
-                    } else {
-                        uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (size_t)tok * p.n_feat + feat;
-                        const uint32_t lo = f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
-                        const uint32_t hi = f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
-                        *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
-                    }
+                for (int v = 0; v < 4; ++v) {
+                    const float a = acc[0][i][j][4 * g + v];
+                    if constexpr (EPI == kEpiSwiGLU) r[v] = silu(a) * acc[NB - 1][i][j][4 * g + v];
+                    else r[v] = a;
                 }
+                store_run<T, NB, EPI>(p, tok, feat, r);
             }
         }
     }
 }
 
-// Tile table: one entry per token tile, (expert, first token tile of that expert, first
-// row, rows of the expert).  Single workgroup; E <= 1024.
-// Segments are clipped to [0, rows) so malformed offsets can never address past the
-// buffers, and no more than `capacity` entries are written.
-__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets, int E,
-                                                          int rows, int btok, int capacity,
-                                                          int4* table, int* count) {
+// Dense product (the gate logits): one expert, rows [0, dense_rows), XCD-contiguous tiles.
+template <typename T, int NB, int EPI, int BT, int BF, int S>
+__global__ __launch_bounds__(kThreads, 1) void dense_gemm_kernel(GemmParams<T, NB> p) {
+    __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, NB, S>::kLdsBytes];
+    const int ntt = (p.dense_rows + BT - 1) / BT;
+    const int total = ntt * p.feat_tiles;
+    const int chunk = (total + 7) >> 3;
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    if (local >= chunk) return;
+    const int L = xcd * chunk + local;
+    if (L >= total) return;
+    const int ftile = L / ntt, ttile = L - ftile * ntt;
+    compute_tile<T, NB, EPI, BT, BF, S>(p, lds, 0, ttile * BT, min(p.dense_rows, p.act_rows),
+                                        ftile * BF);
+}
+
+// Grouped expert product.  XCD x (workgroups x, x + 8, ...) takes a contiguous share of
+// the tiles in dispatch order.  Tiles of one expert go in blocks of kGroupTok token tiles;
+// inside a block the feature tile varies slowest, so the ~32 tiles an XCD runs at once
+// cover about 4 token tiles x 8 feature tiles and share both operands through its L2.
+template <typename T, int NB, int EPI, int BT, int BF, int S>
+__global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, NB> p) {
+    __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, NB, S>::kLdsBytes];
+    const int total = *p.table_count * p.feat_tiles;
+    const int chunk = (total + 7) >> 3;
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    if (local >= chunk) return;
+    const int L = xcd * chunk + local;
+    if (L >= total) return;
+    const int4 te = p.table[L / p.feat_tiles];
+    const int expert = te.x, first = te.y, seg0 = te.z, segn = te.w;
+    const int n_e = (segn + BT - 1) / BT;
+    const int q = L - p.feat_tiles * first;
+    const int blk_tiles = kGroupTok * p.feat_tiles;
+    const int blk = min(q / blk_tiles, (n_e - 1) / kGroupTok);
+    const int width = min(kGroupTok, n_e - blk * kGroupTok);
+    const int ql = q - blk * blk_tiles;
+    const int ftile = ql / width;
+    const int ttile = blk * kGroupTok + (ql - ftile * width);
+    compute_tile<T, NB, EPI, BT, BF, S>(p, lds, expert, seg0 + ttile * BT,
+                                        min(seg0 + segn, p.act_rows), ftile * BF);
+}
+
+// Tile table, built on the device from the offsets (no host read of the counts): one
+// entry per BT-row token tile of every expert, (expert, first token tile of that expert,
+// first row, rows); *count = entries.  Segments are clipped to [0, rows) so malformed
+// offsets can never address past the buffers, and no more than cap entries are written.
+// Single workgroup; E <= 1024.
+__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets, int E, int rows,
+                                                          int btok, int cap, int4* table,
+                                                          int* count) {
     __shared__ int scan[2][1024];
     const int e = threadIdx.x;
-    int beg = 0, cnt = 0, n = 0;
+    int beg = 0, cnt = 0, nt = 0;
     if (e < E) {
         beg = min(max(offsets[e], 0), rows);
         cnt = max(min(offsets[e + 1], rows) - beg, 0);
-        n = (cnt + btok - 1) / btok;
+        nt = (cnt + btok - 1) / btok;
     }
-    // inclusive Hillis-Steele scan of n over the block
+    // inclusive Hillis-Steele scan of the tile counts
     int cur = 0;
-    scan[0][e] = n;
+    scan[0][e] = nt;
     __syncthreads();
     for (int d = 1; d < 1024; d <<= 1) {
         const int v = scan[cur][e] + (e >= d ? scan[cur][e - d] : 0);
@@ -322,17 +361,24 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets
         cur ^= 1;
         __syncthreads();
     }
-    const int incl = scan[cur][e];
-    const int first = incl - n;
-    for (int j = 0; j < n && first + j < capacity; ++j) table[first + j] = make_int4(e, first, beg, cnt);
-    if (e == 1023) *count = min(incl, capacity);
+    const int first = scan[cur][e] - nt;
+    for (int j = 0; j < nt && first + j < cap; ++j) table[first + j] = make_int4(e, first, beg, cnt);
+    if (e == 1023) *count = min(scan[cur][e], cap);
 }
 
 template <typename T, int NB, int EPI, int BT, int BF, int S>
-hipError_t launch_gemm(const GemmParams<T, NB>& p, int grid, hipStream_t s) {
+hipError_t launch_dense(const GemmParams<T, NB>& p, int grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
     grid = (grid + 7) & ~7;
-    hipLaunchKernelGGL((gemm_nt_kernel<T, NB, EPI, BT, BF, S>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((dense_gemm_kernel<T, NB, EPI, BT, BF, S>), dim3(grid), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int NB, int EPI, int BT, int BF, int S>
+hipError_t launch_expert(const GemmParams<T, NB>& p, int max_tiles, hipStream_t s) {
+    const int grid = (max_tiles + 7) & ~7;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((expert_gemm_kernel<T, NB, EPI, BT, BF, S>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -348,13 +394,30 @@ hipError_t gate_logits_t(int T_, int H, int E, const void* x, const void* wg, co
     p.w_stride = 0;
     p.n_feat = E;
     p.feat_tiles = (E + BF - 1) / BF;
-    p.table = nullptr;
-    p.table_count = nullptr;
     p.dense_rows = T_;
     p.out = logits;
     p.bias = bias;
     const int grid = ((T_ + BT - 1) / BT) * p.feat_tiles;
-    return launch_gemm<T, 1, kEpiLogits, BT, BF, S>(p, grid, s);
+    return launch_dense<T, 1, kEpiLogits, BT, BF, S>(p, grid, s);
+}
+
+struct TableLayout {
+    int* count;
+    int4* table;
+    int cap;
+};
+
+__host__ __device__ inline long long tiles_cap(long long N, int E) {
+    return (N + kExpertBTok - 1) / kExpertBTok + (E < N ? E : N);
+}
+
+inline TableLayout carve_tables(void* ws, int N, int E) {
+    TableLayout t;
+    char* w = static_cast<char*>(ws);
+    t.count = reinterpret_cast<int*>(w);
+    t.cap = (int)tiles_cap(N, E);
+    t.table = reinterpret_cast<int4*>(w + 256);
+    return t;
 }
 
 template <typename T>
@@ -362,11 +425,9 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
                      const void* w1, const void* w3, const void* w2, void* h, void* y, void* ws,
                      hipStream_t s) {
     constexpr int BT = kExpertBTok;
-    int* count = static_cast<int*>(ws);
-    int4* table = reinterpret_cast<int4*>(static_cast<char*>(ws) + 256);
-    const int tok_tiles_max = (N + BT - 1) / BT + (E < N ? E : N);
-    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, N, BT,
-                       tok_tiles_max, table, count);
+    const TableLayout tl = carve_tables(ws, N, E);
+    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, N, BT, tl.cap,
+                       tl.table, tl.count);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
@@ -380,10 +441,11 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
     up.w_stride = (long long)F * H;
     up.n_feat = F;
     up.feat_tiles = (F + UP_BF - 1) / UP_BF;
-    up.table = table;
-    up.table_count = count;
+    up.table = tl.table;
+    up.table_count = tl.count;
     up.out = h;
-    err = launch_gemm<T, 2, kEpiSwiGLU, BT, UP_BF, STAGES>(up, tok_tiles_max * up.feat_tiles, s);
+    err = launch_expert<T, 2, kEpiSwiGLU, BT, UP_BF, STAGES>(
+        up, tl.cap * up.feat_tiles, s);
     if (err != hipSuccess) return err;
 
     GemmParams<T, 1> dn{};
@@ -394,17 +456,17 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
     dn.w_stride = (long long)H * F;
     dn.n_feat = H;
     dn.feat_tiles = (H + DN_BF - 1) / DN_BF;
-    dn.table = table;
-    dn.table_count = count;
+    dn.table = tl.table;
+    dn.table_count = tl.count;
     dn.out = y;
-    return launch_gemm<T, 1, kEpiStore, BT, DN_BF, STAGES>(dn, tok_tiles_max * dn.feat_tiles, s);
+    return launch_expert<T, 1, kEpiStore, BT, DN_BF, STAGES>(
+        dn, tl.cap * dn.feat_tiles, s);
 }
 
 }  // namespace
 
 size_t gemm_ws_bytes(long long N, int E) {
-    const long long tiles = (N + kExpertBTok - 1) / kExpertBTok + (E < N ? E : N);
-    return 256 + (size_t)tiles * sizeof(int4);
+    return 256 + (size_t)tiles_cap(N, E) * sizeof(int4);
 }
 
 hipError_t launch_gate_logits(int dt, int T, int H, int E, const void* x, const void* wg,
