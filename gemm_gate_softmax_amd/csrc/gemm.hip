@@ -29,11 +29,20 @@ enum Epilogue { kEpiLogits = 0, kEpiSwiGLU = 1, kEpiStore = 2 };
 // product 256 features; a 3-slot ring of 48 KiB k-slices (64 k per row, whole 128-byte
 // lines).  The gate logits use small 64 x 64 tiles so a few thousand tokens still fill
 // the chip.
-constexpr int kExpertBTok = 128;
-constexpr int kExpertUpBF = 128;
-constexpr int kExpertDownBF = 256;
-constexpr int kExpertStages = 3;
-constexpr int kGroupTok = 4;      // token tiles per L2-sharing block (see expert_tile_of)
+#ifndef MOE_EXPERT_BTOK
+#define MOE_EXPERT_BTOK 128
+#define MOE_EXPERT_UP_BF 128
+#define MOE_EXPERT_DOWN_BF 256
+#define MOE_EXPERT_STAGES 3
+#define MOE_EXPERT_RB 128
+#define MOE_GROUP_TOK 4
+#endif
+constexpr int kExpertBTok = MOE_EXPERT_BTOK;
+constexpr int kExpertUpBF = MOE_EXPERT_UP_BF;
+constexpr int kExpertDownBF = MOE_EXPERT_DOWN_BF;
+constexpr int kExpertStages = MOE_EXPERT_STAGES;
+constexpr int kExpertRowBytes = MOE_EXPERT_RB;
+constexpr int kGroupTok = MOE_GROUP_TOK;      // token tiles per L2-sharing block (see expert_tile_of)
 
 template <typename T, int NB>
 struct GemmParams {
@@ -99,40 +108,39 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
     __builtin_amdgcn_s_barrier();
 }
 
-// Runtime number of stages still allowed in flight (0..M) -> compile-time wait.
-template <int DMA, int M, bool LGKM>
-__device__ __forceinline__ void wait_stages(int m) {
-    if constexpr (M == 0) {
-        wait_vm_and_barrier<0, LGKM>();
-    } else {
-        if (m >= M) wait_vm_and_barrier<M * DMA, LGKM>();
-        else wait_stages<DMA, M - 1, LGKM>(m);
-    }
-}
-
 // LDS layout: a stage holds BT activation rows then NB*BF weight rows, RB bytes each
-// (RB = 128: whole cache lines, so every DMA instruction issues full-line L2 requests;
-// half-line requests measured ~30% slower at the L2), unpadded.  The 16-byte chunk c of
-// row r sits in slot c ^ (r & 7), which reads as fast as fully contiguous data for the
-// 32x32 fragment pattern (lane l: row r0 + l % 32, chunk c0 + l / 32).
-template <int BT, int BF, int NB, int S>
+// (RB = 128: whole cache lines; RB = 64: half lines, which halves a stage so the ring can
+// be deeper), unpadded.  The 16-byte chunk c of row r sits in slot c ^ swz(r).  The LDS
+// serves a 16-byte-per-lane read 16 lanes at a time from 64 four-byte banks, so the 16
+// rows a fragment read touches at once (lane l: row r0 + l % 32, chunk c0 + l / 32) must
+// land on 16 distinct 16-byte bank groups of a 256-byte window: rows r and r + 8 (128-byte
+// rows) or r and r + 4 (64-byte rows) share the window position and differ in swz(r).
+// Measured: 200 B/clk per CU, as fast as contiguous reads; c ^ (r & 7) reached 113.
+template <int BT, int BF, int NB, int S, int RB>
 struct CompTile {
-    static constexpr int kRowBytes = 128;                   // bytes of K per row and stage
+    static_assert(RB == 64 || RB == 128, "row bytes");
+    static constexpr int kRowBytes = RB;                    // bytes of K per row and stage
     static constexpr int kRows = BT + NB * BF;              // LDS rows per stage
     static constexpr int kStageBytes = kRows * kRowBytes;
     static constexpr int kLdsBytes = S * kStageBytes;
 };
 
+template <int RB>
+__device__ __forceinline__ int chunk_swizzle(int r) {
+    return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+
 // One compute tile: activation rows [row0, row0 + BT) (stored below row_end) against
 // weight rows [f0, f0 + BF) of each operand of `expert`.
-template <typename T, int NB, int EPI, int BT, int BF, int S>
+template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool FULL>
 __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* lds, int expert,
                                              int row0, int row_end, int f0) {
-    constexpr int kRowBytes = CompTile<BT, BF, NB, S>::kRowBytes;
+    using Tile = CompTile<BT, BF, NB, S, RB>;
+    constexpr int kRowBytes = Tile::kRowBytes;
     constexpr int kRowsPerDma = 1024 / kRowBytes;    // rows per 1 KiB DMA instruction
     constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
-    constexpr int kRows = CompTile<BT, BF, NB, S>::kRows;
-    constexpr int kStageBytes = CompTile<BT, BF, NB, S>::kStageBytes;
+    constexpr int kRows = Tile::kRows;
+    constexpr int kStageBytes = Tile::kStageBytes;
     constexpr int kDma = kRows / (4 * kRowsPerDma);  // DMA instructions per wave per stage
     constexpr int TT = BT / 64, FT = BF / 64;        // 32x32 tiles per wave (tokens, features)
     constexpr int KS = kRowBytes / 32;               // k-steps (16-byte chunk pairs) per stage
@@ -154,7 +162,7 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
     for (int i = 0; i < kDma; ++i) {
         const int rl = lane / kChunks;                                // row within the block
         const int r = (wave + 4 * i) * kRowsPerDma + rl;              // row within the stage
-        const int c = (lane % kChunks) ^ (rl & 7);                    // chunk held by this slot
+        const int c = (lane % kChunks) ^ chunk_swizzle<RB>(r);        // chunk held by this slot
         if (i < BT / kBlkRows) {
             const int ar = min(row0 + r, p.act_rows - 1);
             src[i] = reinterpret_cast<const char*>(p.act) + (size_t)ar * row_bytes + c * 16;
@@ -181,7 +189,11 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
     // as TT x FT tiles of 32 x 32 (MFMA rows = features, MFMA columns = tokens) ----
     const int wt = wave & 1, wf = wave >> 1;
     const int l32 = lane & 31, lhalf = lane >> 5;
-    const int swz = l32 & 7;                      // row & 7 for every fragment row
+    const int swz = chunk_swizzle<RB>(l32);       // fragment rows start at multiples of 32
+    // A tile that is not FULL (an expert's last, or only, token tile) skips the MFMAs of
+    // 32-token column tiles holding no row below row_end: for an expert with a handful of
+    // rows most of the tile's MFMA work, so it runs at the speed of its weight stream.
+    const int jn = FULL ? TT : (min(max(row_end - (row0 + wt * (BT / 2)), 0), BT / 2) + 31) / 32;
     f32x16_t acc[NB][FT][TT];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -213,18 +225,44 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
     do {                                                                                     \
         _Pragma("unroll") for (int b = 0; b < NB; ++b)                                       \
             _Pragma("unroll") for (int i = 0; i < FT; ++i)                                   \
-                _Pragma("unroll") for (int j = 0; j < TT; ++j) Mfma<T>::mac(acc[b][i][j], FW[b][i], FA[j]); \
+                _Pragma("unroll") for (int j = 0; j < TT; ++j)                               \
+                    if (FULL || j < jn) Mfma<T>::mac(acc[b][i][j], FW[b][i], FA[j]);         \
     } while (0)
     static_assert(KS % 2 == 0, "k-steps alternate between the two fragment buffers");
 
-    // DMA for stage kt+S-1 is spread over the KS k-steps of stage kt (a quarter per
-    // k-step) into the slot stage kt-1 vacated, so requests leave each wave steadily
-    // rather than in one burst at the barrier.
+    // The DMA for stage kt+S-1 goes into the slot stage kt-1 vacated and is interleaved
+    // with the MFMAs of stage kt, one instruction every few MFMAs: a burst of transfers
+    // can fill the memory pipeline's queue, and a wave blocked on issuing one cannot
+    // issue the MFMAs behind it.  Stage indices are clamped to the last stage, so the
+    // loop issues the same number of transfers every iteration (a redundant copy of the
+    // last stage lands in a slot no later stage reads) and every wait count is constant.
     static_assert(kDma % KS == 0, "DMA instructions split evenly over the k-steps");
-    constexpr int kPart = kDma / KS;
+    constexpr int kPerStep = kDma / KS;                 // DMA instructions per k-step
+    constexpr int kNm = NB * FT * TT;                   // MFMAs per k-step
+    // At the end-of-stage wait of stage kt the newest stage, kt+S-1, has issued all but
+    // its last k-step's part, so "stage kt+1 landed" allows the S-3 full stages between
+    // them plus that partial stage to remain in flight.
+    static_assert(S >= 3, "the last k-step's transfers are issued after the stage wait");
+    constexpr int kInFlight = (S - 2) * kDma - kPerStep;
+#define MOE_MFMAS_DMA(FA, FW, Q0)                                                             \
+    do {                                                                                     \
+        _Pragma("unroll") for (int b = 0; b < NB; ++b)                                       \
+            _Pragma("unroll") for (int i = 0; i < FT; ++i)                                   \
+                _Pragma("unroll") for (int j = 0; j < TT; ++j) {                             \
+            const int m_ = (b * FT + i) * TT + j;                                            \
+            if (FULL || j < jn) Mfma<T>::mac(acc[b][i][j], FW[b][i], FA[j]);                 \
+            _Pragma("unroll") for (int q_ = 0; q_ < kPerStep; ++q_) {                        \
+                if (m_ == ((q_ + 1) * kNm) / kPerStep - 1) {                                 \
+                    __builtin_amdgcn_sched_barrier(0);                                       \
+                    dma16(src[(Q0) + q_] + doff, dbase + ((Q0) + q_) * 4096);                \
+                    __builtin_amdgcn_sched_barrier(0);                                       \
+                }                                                                            \
+            }                                                                                \
+        }                                                                                    \
+    } while (0)
     const int nk = (int)(row_bytes / kRowBytes);
-    for (int s = 0; s < S - 1 && s < nk; ++s) MOE_ISSUE(s, s, 0, kDma);
-    wait_stages<kDma, S - 2, false>(min(S - 2, nk - 1));          // stage 0 landed
+    for (int s = 0; s < S - 1; ++s) MOE_ISSUE(min(s, nk - 1), s, 0, kDma);
+    wait_vm_and_barrier<(S - 2) * kDma, false>();                 // stage 0 landed
     MOE_LOAD_FRAGS(lds, 0, fa0, fw0);
     // The last stage is peeled off so every loop iteration has the same shape (otherwise
     // the compiler's wait insertion merges paths and drains the prefetched fragments).
@@ -232,24 +270,23 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
     for (int kt = 0; kt < nk - 1; ++kt) {
         const char* st = lds + slot * kStageBytes;
         const int next = slot == S - 1 ? 0 : slot + 1;
-        const bool more = kt + S - 1 < nk;
+        const uint32_t dbase = __builtin_amdgcn_readfirstlane(lds_base + refill * kStageBytes + wave * 1024);
+        const size_t doff = (size_t)min(kt + S - 1, nk - 1) * kRowBytes;
 #pragma unroll
         for (int ks = 0; ks < KS; ks += 2) {
             MOE_LOAD_FRAGS(st, ks + 1, fa1, fw1);
-            if (more) MOE_ISSUE(kt + S - 1, refill, ks * kPart, kPart);
             __builtin_amdgcn_sched_barrier(0);
-            MOE_MFMAS(fa0, fw0);
+            MOE_MFMAS_DMA(fa0, fw0, ks * kPerStep);
             __builtin_amdgcn_sched_barrier(0);
-            if (more) MOE_ISSUE(kt + S - 1, refill, (ks + 1) * kPart, kPart);
             if (ks + 2 < KS) {
                 MOE_LOAD_FRAGS(st, ks + 2, fa0, fw0);
             } else {
                 // this wave's reads of stage kt are complete; stage kt+1 landed everywhere
-                wait_stages<kDma, (S >= 2 ? S - 2 : 0), true>(min(S - 2, nk - 2 - kt));
+                wait_vm_and_barrier<kInFlight, true>();
                 MOE_LOAD_FRAGS(lds + next * kStageBytes, 0, fa0, fw0);
             }
             __builtin_amdgcn_sched_barrier(0);
-            MOE_MFMAS(fa1, fw1);
+            MOE_MFMAS_DMA(fa1, fw1, (ks + 1) * kPerStep);
             __builtin_amdgcn_sched_barrier(0);
         }
         slot = next;
@@ -265,8 +302,12 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
             MOE_MFMAS(fa1, fw1);
         }
     }
+    // redundant copies of the last stage may still be landing; the workgroup's LDS must
+    // be quiet before it ends
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
 #undef MOE_LOAD_FRAGS
 #undef MOE_MFMAS
+#undef MOE_MFMAS_DMA
 #undef MOE_ISSUE
 
     // ---- epilogue: lane holds one token and, per 32-feature tile, 4 runs of 4 features ----
@@ -293,9 +334,9 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
 }
 
 // Dense product (the gate logits): one expert, rows [0, dense_rows), XCD-contiguous tiles.
-template <typename T, int NB, int EPI, int BT, int BF, int S>
+template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
 __global__ __launch_bounds__(kThreads, 1) void dense_gemm_kernel(GemmParams<T, NB> p) {
-    __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, NB, S>::kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, NB, S, RB>::kLdsBytes];
     const int ntt = (p.dense_rows + BT - 1) / BT;
     const int total = ntt * p.feat_tiles;
     const int chunk = (total + 7) >> 3;
@@ -304,17 +345,20 @@ __global__ __launch_bounds__(kThreads, 1) void dense_gemm_kernel(GemmParams<T, N
     const int L = xcd * chunk + local;
     if (L >= total) return;
     const int ftile = L / ntt, ttile = L - ftile * ntt;
-    compute_tile<T, NB, EPI, BT, BF, S>(p, lds, 0, ttile * BT, min(p.dense_rows, p.act_rows),
-                                        ftile * BF);
+    const int row_end = min(p.dense_rows, p.act_rows);
+    if (row_end - ttile * BT >= BT)
+        compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, 0, ttile * BT, row_end, ftile * BF);
+    else
+        compute_tile<T, NB, EPI, BT, BF, S, RB, false>(p, lds, 0, ttile * BT, row_end, ftile * BF);
 }
 
 // Grouped expert product.  XCD x (workgroups x, x + 8, ...) takes a contiguous share of
 // the tiles in dispatch order.  Tiles of one expert go in blocks of kGroupTok token tiles;
 // inside a block the feature tile varies slowest, so the ~32 tiles an XCD runs at once
 // cover about 4 token tiles x 8 feature tiles and share both operands through its L2.
-template <typename T, int NB, int EPI, int BT, int BF, int S>
+template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
 __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, NB> p) {
-    __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, NB, S>::kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, NB, S, RB>::kLdsBytes];
     const int total = *p.table_count * p.feat_tiles;
     const int chunk = (total + 7) >> 3;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
@@ -331,8 +375,11 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, 
     const int ql = q - blk * blk_tiles;
     const int ftile = ql / width;
     const int ttile = blk * kGroupTok + (ql - ftile * width);
-    compute_tile<T, NB, EPI, BT, BF, S>(p, lds, expert, seg0 + ttile * BT,
-                                        min(seg0 + segn, p.act_rows), ftile * BF);
+    const int row0 = seg0 + ttile * BT, row_end = min(seg0 + segn, p.act_rows);
+    if (row_end - row0 >= BT)
+        compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, expert, row0, row_end, ftile * BF);
+    else
+        compute_tile<T, NB, EPI, BT, BF, S, RB, false>(p, lds, expert, row0, row_end, ftile * BF);
 }
 
 // Tile table, built on the device from the offsets (no host read of the counts): one
@@ -366,19 +413,19 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets
     if (e == 1023) *count = min(scan[cur][e], cap);
 }
 
-template <typename T, int NB, int EPI, int BT, int BF, int S>
+template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
 hipError_t launch_dense(const GemmParams<T, NB>& p, int grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
     grid = (grid + 7) & ~7;
-    hipLaunchKernelGGL((dense_gemm_kernel<T, NB, EPI, BT, BF, S>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((dense_gemm_kernel<T, NB, EPI, BT, BF, S, RB>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
-template <typename T, int NB, int EPI, int BT, int BF, int S>
+template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
 hipError_t launch_expert(const GemmParams<T, NB>& p, int max_tiles, hipStream_t s) {
     const int grid = (max_tiles + 7) & ~7;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((expert_gemm_kernel<T, NB, EPI, BT, BF, S>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((expert_gemm_kernel<T, NB, EPI, BT, BF, S, RB>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -398,7 +445,7 @@ hipError_t gate_logits_t(int T_, int H, int E, const void* x, const void* wg, co
     p.out = logits;
     p.bias = bias;
     const int grid = ((T_ + BT - 1) / BT) * p.feat_tiles;
-    return launch_dense<T, 1, kEpiLogits, BT, BF, S>(p, grid, s);
+    return launch_dense<T, 1, kEpiLogits, BT, BF, S, 128>(p, grid, s);
 }
 
 struct TableLayout {
@@ -431,7 +478,8 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
-    constexpr int UP_BF = kExpertUpBF, DN_BF = kExpertDownBF, STAGES = kExpertStages;
+    constexpr int UP_BF = kExpertUpBF, DN_BF = kExpertDownBF, STAGES = kExpertStages,
+                  RB = kExpertRowBytes;
     GemmParams<T, 2> up{};
     up.act = static_cast<const T*>(xd);
     up.act_rows = N;
@@ -444,7 +492,7 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
     up.table = tl.table;
     up.table_count = tl.count;
     up.out = h;
-    err = launch_expert<T, 2, kEpiSwiGLU, BT, UP_BF, STAGES>(
+    err = launch_expert<T, 2, kEpiSwiGLU, BT, UP_BF, STAGES, RB>(
         up, tl.cap * up.feat_tiles, s);
     if (err != hipSuccess) return err;
 
@@ -459,7 +507,7 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
     dn.table = tl.table;
     dn.table_count = tl.count;
     dn.out = y;
-    return launch_expert<T, 1, kEpiStore, BT, DN_BF, STAGES>(
+    return launch_expert<T, 1, kEpiStore, BT, DN_BF, STAGES, RB>(
         dn, tl.cap * dn.feat_tiles, s);
 }
 
