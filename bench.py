@@ -9,12 +9,21 @@ per-stage table goes to stderr first.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config xmoe_large]
                   [--no-cpu-baseline] [--cpu-seconds 15]
+  python bench.py --calibrate-copy     # plain 1 GiB device copies, for HBM byte counters
+
+The roofline object covers the dominant kernel, the expert gate/up product with its
+SwiGLU epilogue (two thirds of the layer's flops), timed on its own through the same
+entry point with w2 = y = NULL.  Its "traffic" (HBM bytes per launch from FETCH_SIZE and
+WRITE_SIZE counters, scaled by a plain copy's reading) comes from the committed counter
+summary and is reported only while the kernel sources still hash to what was profiled.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -24,6 +33,10 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer fwd tokens/s + grouped-GEMM % MFMA peak, X-MoE Large, 1 GPU"
 HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, published
+UP_KERNEL = "expert_gemm_kernel<moe::bf16_t, 2, 1"   # name prefix in profiler output
+KERNEL_SOURCES = ("gemm_gate_softmax_amd/csrc/gemm.hip", "gemm_gate_softmax_amd/csrc/device.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "xmoe_large_expert_up_traffic.md")
+COPY_BYTES = 1 << 30
 
 
 def log(msg):
@@ -41,7 +54,44 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run plain device copies of 1 GiB (counter calibration)")
     return ap.parse_args()
+
+
+def kernel_digest():
+    """sha256 over the expert kernel's sources: counter readings are tied to it."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch of the up kernel from the committed counter summary, or None
+    when it is missing, for another workload, or taken from other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, re.M))
+    if fields.get("workload") != workload or fields.get("source_sha256") != kernel_digest():
+        return None
+    return int(fields["hbm_bytes_per_launch"])
+
+
+def calibrate_copy():
+    import torch
+    src = torch.full((COPY_BYTES,), 7, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": COPY_BYTES,
+                      "bytes_written": COPY_BYTES, "launches": 3}), flush=True)
+    return 0
 
 
 def algorithmic(cfg, counts):
@@ -52,6 +102,7 @@ def algorithmic(cfg, counts):
     return dict(
         active_experts=active,
         gemm_flops=6.0 * N * H * F,
+        up_flops=4.0 * N * H * F,
         gemm_bytes=active * 3.0 * H * F * b + b * (2.0 * N * H + 2.0 * N * F),
         dispatch_bytes=b * (T * H + N * H) + 4.0 * N,
         combine_bytes=b * (N * H + T * H) + 8.0 * N,
@@ -119,7 +170,9 @@ def main():
         log("bench.py: only --gpus 1 is supported (single-GPU layer forward)")
         return 2
 
-    import numpy as np
+    if args.calibrate_copy:
+        return calibrate_copy()
+
     import torch
 
     from gemm_gate_softmax_amd import ops
@@ -174,9 +227,16 @@ def main():
         fn()
         torch.cuda.synchronize()
         st_ms[name] = time_calls(fn, args.steps, stream)
+    # The dominant kernel alone: the gate/up product (tile table + one expert launch).
+    up_call = lambda: ops.moe_grouped_gemm_swiglu(bufs["xd"], bufs["offsets"], d["w1"], d["w3"],
+                                                  None, h=bufs["h"], ws=gws)
+    up_call()
+    torch.cuda.synchronize()
+    up_ms = time_calls(up_call, args.steps, stream)
     alg = algorithmic(cfg, counts)
     g_ms = st_ms["grouped_gemm"]
     tflops = alg["gemm_flops"] / (g_ms * 1e-3) / 1e12
+    up_tflops = alg["up_flops"] / (up_ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[cfg.dtype]
     stage_report = {n: round(v * 1e3, 2) for n, v in st_ms.items()}
     bw = {
@@ -187,6 +247,7 @@ def main():
     if args.verbose:
         for n, v in st_ms.items():
             log(f"  {n:13s} {v * 1e3:9.1f} us")
+        log(f"  up kernel     {up_ms * 1e3:9.1f} us  {up_tflops:.1f} TFLOP/s")
         log(f"  grouped GEMM {tflops:.1f} TFLOP/s = {100 * tflops / peak:.1f}% of {peak} "
             f"(weights+activations {bw['grouped_gemm_GBs']:.0f} GB/s); dispatch "
             f"{bw['dispatch_GBs']:.0f} GB/s, combine {bw['combine_GBs']:.0f} GB/s")
@@ -200,10 +261,15 @@ def main():
                    "k": cfg.k, "gate_bias": None if cfg.bias is None else f"{cfg.bias[0]}({cfg.bias[1]})",
                    "seed": args.seed, "active_experts": alg["active_experts"],
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None,
-                     "kernel": "moe_grouped_gemm_swiglu (tile table + gate/up SwiGLU + down)"},
-        "stages_us": stage_report,
+        "roofline": {"bound": "mfma", "achieved": round(up_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(up_tflops / peak, 4),
+                     "traffic": recorded_traffic(cfg.name),
+                     "kernel": "expert_gemm_kernel, gate/up product + SwiGLU "
+                               f"({alg['up_flops']:.4g} flop per launch, {up_ms * 1e3:.1f} us)",
+                     "source_sha256": kernel_digest()},
+        "grouped_gemm": {"tflops": round(tflops, 2), "frac_mfma": round(tflops / peak, 4),
+                         "us": round(g_ms * 1e3, 1)},
+        "stages_us": stage_report | {"up_kernel": round(up_ms * 1e3, 2)},
         "bandwidth": {k_: round(v, 1) for k_, v in bw.items()}
         | {"dispatch_frac_hbm": round(bw["dispatch_GBs"] / HBM_PEAK_GBS, 4),
            "combine_frac_hbm": round(bw["combine_GBs"] / HBM_PEAK_GBS, 4),

@@ -129,8 +129,10 @@ MOE_API moe_status_t moe_grouped_gemm_swiglu(moe_dtype_t dt, int N, int E, int H
     if (E > MOE_E_MAX) return MOE_ERR_UNSUPPORTED;
     MOE_TRY(check_dim(H));
     MOE_TRY(check_dim(F));
+    if ((w2 == nullptr) != (y == nullptr)) return MOE_ERR_INVALID_VALUE;
     if (N == 0) return MOE_OK;
-    MOE_TRY(check_ptrs({xd, offsets, w1, w3, w2, h, y, ws}));
+    MOE_TRY(check_ptrs({xd, offsets, w1, w3, h, ws}));
+    if (w2) MOE_TRY(check_ptrs({w2, y}));
     if (ws_bytes < gemm_ws(N, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     return launched(moe::launch_grouped_gemm(dt, N, E, H, F, xd, offsets, w1, w3, w2, h, y, ws,
                                              as_stream(stream)));

@@ -494,7 +494,7 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
     up.out = h;
     err = launch_expert<T, 2, kEpiSwiGLU, BT, UP_BF, STAGES, RB>(
         up, tl.cap * up.feat_tiles, s);
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || w2 == nullptr) return err;      // up product only
 
     GemmParams<T, 1> dn{};
     dn.act = static_cast<const T*>(h);

@@ -181,16 +181,24 @@ def moe_dispatch(x, dest_pos, xd=None, stream=None):
 
 
 def moe_grouped_gemm_swiglu(xd, offsets, w1, w3, w2, h=None, y=None, ws=None, stream=None):
-    """SwiGLU experts over the ragged segments.  Returns (h [N,F], y [N,H])."""
+    """SwiGLU experts over the ragged segments.  Returns (h [N,F], y [N,H]).
+
+    w2=None computes only h (the gate/up product and its SwiGLU) and returns (h, None).
+    """
     dt = dtype_code(xd.dtype)
     N, H = xd.shape
     E, F = w1.shape[0], w1.shape[1]
     _need(xd, "xd"), _need(offsets, "offsets", torch.int32, (E + 1,))
     _need(w1, "w1", xd.dtype, (E, F, H)), _need(w3, "w3", xd.dtype, (E, F, H))
-    _need(w2, "w2", xd.dtype, (E, H, F))
+    if w2 is not None:
+        _need(w2, "w2", xd.dtype, (E, H, F))
     h = torch.empty((N, F), dtype=xd.dtype, device=xd.device) if h is None else h
-    y = torch.empty((N, H), dtype=xd.dtype, device=xd.device) if y is None else y
-    _need(h, "h", xd.dtype, (N, F)), _need(y, "y", xd.dtype, (N, H))
+    _need(h, "h", xd.dtype, (N, F))
+    if w2 is None:
+        y = None
+    else:
+        y = torch.empty((N, H), dtype=xd.dtype, device=xd.device) if y is None else y
+        _need(y, "y", xd.dtype, (N, H))
     if ws is None:  # sized for N = T*k rows: pass T = N, k = 1
         ws = workspace(MOE_WS_GEMM, N, H, E, F, 1, dt, xd.device)
     _check("moe_grouped_gemm_swiglu", lib().moe_grouped_gemm_swiglu(

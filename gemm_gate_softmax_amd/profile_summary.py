@@ -1,0 +1,136 @@
+"""Summaries of rocprofv3 CSV output for this library's kernels (text for profiles/).
+
+  python -m gemm_gate_softmax_amd.profile_summary stats KERNEL_STATS.csv --command "..."
+      Markdown table of a ``rocprofv3 --kernel-trace --stats --output-format csv`` run.
+
+  python -m gemm_gate_softmax_amd.profile_summary traffic --kernel PREFIX --workload NAME \\
+      --fetch BENCH_FETCH.csv --write BENCH_WRITE.csv \\
+      --copy-fetch COPY_FETCH.csv --copy-write COPY_WRITE.csv --copy-bytes B --command "..."
+      HBM bytes per launch of one kernel from ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``
+      runs (KiB per dispatch), each scaled by what the same counter reads for a plain
+      device copy of B bytes (the copy kernel is the largest dispatch of its run).
+
+Only the standard library is used; nothing here touches the GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ("gemm_gate_softmax_amd/csrc/gemm.hip", "gemm_gate_softmax_amd/csrc/device.h")
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name, width=96):
+    name = name.replace("moe::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+    cut = name.find(">(")
+    if cut > 0:
+        name = name[:cut + 1]
+    return name if len(name) <= width else name[:width - 3] + "..."
+
+
+def kernel_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stats_markdown(path, command, title):
+    rows = sorted(_rows(path), key=lambda r: -float(r["TotalDurationNs"]))
+    out = [f"# {title}", "", "Command (repository root, one MI355X):", "", f"    {command}", "",
+           "`Calls` counts dispatches over the whole run (warm-up, timed steps, per-stage",
+           "timing, input generation); durations are per dispatch.", "",
+           "| kernel | calls | avg (us) | min (us) | max (us) | % of GPU time |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                   f"{float(r['Percentage']):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def _per_dispatch(path, prefix):
+    """Counter value (summed over its instances) for each dispatch of kernels whose name
+    contains prefix."""
+    per = {}
+    for r in _rows(path):
+        if prefix in _short(r["Kernel_Name"], 10**6):
+            d = r["Dispatch_Id"]
+            per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
+    return list(per.values())
+
+
+def _copy_reading(path):
+    """Counter reading (KiB) of the plain copy: the largest dispatch of the run."""
+    per = {}
+    for r in _rows(path):
+        d = r["Dispatch_Id"]
+        per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
+    vals = sorted(per.values())
+    return vals[-1]
+
+
+def traffic_markdown(a):
+    fetch = _per_dispatch(a.fetch, a.kernel)
+    write = _per_dispatch(a.write, a.kernel)
+    if not fetch or not write:
+        raise SystemExit(f"no dispatch of {a.kernel!r} in the counter files")
+    cf, cw = _copy_reading(a.copy_fetch), _copy_reading(a.copy_write)
+    f_scale = a.copy_bytes / (cf * 1024.0)
+    w_scale = a.copy_bytes / (cw * 1024.0)
+    fetch_b = statistics.mean(fetch) * 1024.0 * f_scale
+    write_b = statistics.mean(write) * 1024.0 * w_scale
+    total = int(round(fetch_b + write_b))
+    out = [f"# HBM traffic per launch: {a.kernel} ({a.workload})", "",
+           "Commands (repository root, one MI355X), one counter per run:", ""]
+    out += [f"    {c}" for c in a.command]
+    out += ["",
+            "FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch.  A plain device copy of "
+            f"{a.copy_bytes} bytes reads {cf:.1f} KiB of FETCH_SIZE and {cw:.1f} KiB of WRITE_SIZE, "
+            f"so kernel readings are scaled by {f_scale:.4f} (fetch) and {w_scale:.4f} (write).", "",
+            "| | dispatches | mean reading (KiB) | scaled bytes per launch |",
+            "|---|---|---|---|",
+            f"| fetch | {len(fetch)} | {statistics.mean(fetch):.1f} | {fetch_b:.4g} |",
+            f"| write | {len(write)} | {statistics.mean(write):.1f} | {write_b:.4g} |", "",
+            "Fields read by bench.py (traffic is reported only while the kernel sources hash",
+            "to source_sha256):", "",
+            f"- workload: `{a.workload}`",
+            f"- kernel: `{a.kernel}`",
+            f"- source_sha256: `{kernel_digest()}`",
+            f"- fetch_scale: `{f_scale:.6f}`",
+            f"- write_scale: `{w_scale:.6f}`",
+            f"- hbm_bytes_per_launch: `{total}`", ""]
+    return "\n".join(out)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", default="rocprofv3 kernel summary")
+    t = sub.add_parser("traffic")
+    for k in ("kernel", "workload", "fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--command", action="append", required=True)
+    a = ap.parse_args(argv)
+    sys.stdout.write(stats_markdown(a.csv, a.command, a.title) if a.cmd == "stats"
+                     else traffic_markdown(a))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -119,6 +119,8 @@ moe_status_t moe_dispatch(moe_dtype_t dt, int T, int k, int H, const void *x,
  * xd [N][H], offsets [E+1] (device, as from moe_pft_build), h [N][F], y [N][H].
  * Experts with no rows cost nothing.  ws: moe_workspace_bytes(MOE_WS_GEMM, ...) bytes
  * (holds the device-built tile table; sized from N = T*k and E).
+ * w2 and y both NULL: only h is computed (the gate/up product and its SwiGLU); exactly
+ * one of them NULL is MOE_ERR_INVALID_VALUE.
  */
 moe_status_t moe_grouped_gemm_swiglu(moe_dtype_t dt, int N, int E, int H, int F,
                                      const void *xd, const int32_t *offsets, const void *w1,

@@ -114,6 +114,10 @@ def test_gemm_and_layer_reject(L):
     assert g(1, 100, 8, 64, 64, A, A, A, A, A, A, A, A, 0, None) == WS_SMALL
     assert g(1, 100, 8, 64, 64, A, A, A, MIS, A, A, A, A, 1 << 20, None) == MISALIGNED
     assert g(1, 0, 8, 64, 64, None, None, None, None, None, None, None, None, 0, None) == OK
+    # up product only needs w2 and y both NULL; one of them alone is an error
+    assert g(1, 100, 8, 64, 64, A, A, A, A, None, A, A, A, 1 << 20, None) == INVALID
+    assert g(1, 100, 8, 64, 64, A, A, A, A, A, A, None, A, 1 << 20, None) == INVALID
+    assert g(1, 100, 8, 64, 64, A, A, A, A, None, None, None, A, 1 << 20, None) == INVALID  # h
     lf = L.moe_layer_forward
     bufs = ops.LayerBufs(*([A] * 10))
     args = lambda **kw: [kw.get("dt", 1), kw.get("T", 8), kw.get("H", 64), kw.get("E", 4),

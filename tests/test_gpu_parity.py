@@ -190,6 +190,11 @@ def test_grouped_gemm_parity(orc, dt, N, E, H, F):
     _log(f"gemm {dt} N={N} E={E} H={H} F={F}: h err {eh:.2e} y err {ey:.2e} "
          f"(rms {rms_rel(y, y_ref, dt):.2e})")
     assert eh <= TOL[dt] and ey <= TOL[dt]
+    # the up product alone (w2 = y = NULL) runs the same kernel: identical h
+    h_up, y_up = ops.moe_grouped_gemm_swiglu(dev(xd, dt), dev(offsets), dev(w1, dt),
+                                             dev(w3, dt), None)
+    assert y_up is None
+    assert np.array_equal(host(h_up, dt), h)
 
 
 # ----------------------------------------------------------------------- whole layer
