@@ -21,7 +21,7 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;   // 4 compute waves + 4 loader waves
 
 enum Epilogue { kEpiLogits = 0, kEpiSwiGLU = 1, kEpiStore = 2 };
 
@@ -35,7 +35,7 @@ enum Epilogue { kEpiLogits = 0, kEpiSwiGLU = 1, kEpiStore = 2 };
 #define MOE_EXPERT_DOWN_BF 256
 #define MOE_EXPERT_STAGES 3
 #define MOE_EXPERT_RB 128
-#define MOE_GROUP_TOK 4
+#define MOE_GROUP_TOK 8
 #endif
 constexpr int kExpertBTok = MOE_EXPERT_BTOK;
 constexpr int kExpertUpBF = MOE_EXPERT_UP_BF;
@@ -130,8 +130,16 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
     return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
-// One compute tile: activation rows [row0, row0 + BT) (stored below row_end) against
-// weight rows [f0, f0 + BF) of each operand of `expert`.
+// One tile: activation rows [row0, row0 + BT) (stored below row_end) against weight rows
+// [f0, f0 + BF) of each operand of `expert`, by a workgroup of 8 waves in two roles.
+// Waves 4..7 only move data: each issues its share of every stage's direct-to-LDS
+// transfers into an S-slot ring.  Waves 0..3 only read LDS and issue MFMAs.  A memory
+// instruction waits at issue until the CU's address path (about 64 bytes per clock)
+// accepts it, and a wave stalled there issues nothing else; with the roles split, the
+// compute wave that shares a SIMD with a loader keeps its MFMAs going meanwhile.  One
+// barrier per stage hands the slots over: before barrier kt every loader has seen stage kt
+// land and every compute wave has finished reading stage kt-1, so after it stage kt is
+// read while stage kt+S-1 is loaded into the slot stage kt-1 left.
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool FULL>
 __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* lds, int expert,
                                              int row0, int row_end, int f0) {
@@ -141,58 +149,74 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
     constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
     constexpr int kRows = Tile::kRows;
     constexpr int kStageBytes = Tile::kStageBytes;
-    constexpr int kDma = kRows / (4 * kRowsPerDma);  // DMA instructions per wave per stage
-    constexpr int TT = BT / 64, FT = BF / 64;        // 32x32 tiles per wave (tokens, features)
+    constexpr int kDma = kRows / (4 * kRowsPerDma);  // DMA instructions per loader per stage
+    constexpr int TT = BT / 64, FT = BF / 64;        // 32x32 tiles per compute wave
     constexpr int KS = kRowBytes / 32;               // k-steps (16-byte chunk pairs) per stage
     static_assert(kRows % (4 * kRowsPerDma) == 0 && BT % 64 == 0 && BF % 64 == 0, "tile shape");
     static_assert(BT % (4 * kRowsPerDma) == 0 && BF % (4 * kRowsPerDma) == 0, "operand blocks");
     static_assert(S >= 2 && (S - 2) * kDma < 64 && S * kStageBytes <= 160 * 1024, "ring");
+    static_assert(KS % 2 == 0, "k-steps alternate between the two fragment buffers");
 
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const size_t row_bytes = (size_t)p.K * sizeof(T);
+    const int nk = (int)(row_bytes / kRowBytes);
 
-    // ---- DMA sources: wave w fills row blocks w + 4 i of every stage ----
-    // Block b < BT/kRowsPerDma holds activation rows, the rest weight rows of operand
-    // (4 kRowsPerDma i - BT) / BF: both compile-time once i is unrolled.
-    constexpr int kBlkRows = 4 * kRowsPerDma;                         // rows per i step
-    const char* src[kDma];
+    if (wave >= 4) {
+        // ---- loader: wave 4 + w fills row blocks w + 4 i of every stage.  Block b <
+        // BT/kRowsPerDma holds activation rows, the rest weight rows of operand
+        // (4 kRowsPerDma i - BT) / BF: both compile-time once i is unrolled. ----
+        const int lw = wave - 4;
+        constexpr int kBlkRows = 4 * kRowsPerDma;                     // rows per i step
+        const char* src[kDma];
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) {
-        const int rl = lane / kChunks;                                // row within the block
-        const int r = (wave + 4 * i) * kRowsPerDma + rl;              // row within the stage
-        const int c = (lane % kChunks) ^ chunk_swizzle<RB>(r);        // chunk held by this slot
-        if (i < BT / kBlkRows) {
-            const int ar = min(row0 + r, p.act_rows - 1);
-            src[i] = reinterpret_cast<const char*>(p.act) + (size_t)ar * row_bytes + c * 16;
-        } else {
-            const int b = (kBlkRows * i - BT) / BF;
-            const int f = min(f0 + (r - BT) - b * BF, p.n_feat - 1);
-            src[i] = reinterpret_cast<const char*>(p.w[b] + (size_t)expert * p.w_stride) +
-                     (size_t)f * row_bytes + c * 16;
+        for (int i = 0; i < kDma; ++i) {
+            const int rl = lane / kChunks;                            // row within the block
+            const int r = (lw + 4 * i) * kRowsPerDma + rl;            // row within the stage
+            const int c = (lane % kChunks) ^ chunk_swizzle<RB>(r);    // chunk held by this slot
+            if (i < BT / kBlkRows) {
+                const int ar = min(row0 + r, p.act_rows - 1);
+                src[i] = reinterpret_cast<const char*>(p.act) + (size_t)ar * row_bytes + c * 16;
+            } else {
+                const int b = (kBlkRows * i - BT) / BF;
+                const int f = min(f0 + (r - BT) - b * BF, p.n_feat - 1);
+                src[i] = reinterpret_cast<const char*>(p.w[b] + (size_t)expert * p.w_stride) +
+                         (size_t)f * row_bytes + c * 16;
+            }
         }
+        const uint32_t wbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                                   (__attribute__((address_space(3))) char*)(lds))) + lw * 1024;
+        // all of stage KT into slot SLOT (4 loaders x 1 KiB per 4 KiB block).  Stage indices
+        // are clamped to the last stage, so every iteration issues the same transfers (a
+        // redundant copy lands in a slot no later stage reads) and every wait is constant.
+#define MOE_ISSUE(KT, SLOT)                                                                   \
+        do {                                                                                 \
+            const uint32_t b_ = __builtin_amdgcn_readfirstlane(wbase + (SLOT) * kStageBytes); \
+            const size_t o_ = (size_t)(KT) * kRowBytes;                                      \
+            _Pragma("unroll") for (int i_ = 0; i_ < kDma; ++i_) dma16(src[i_] + o_, b_ + i_ * 4096); \
+        } while (0)
+        for (int s = 0; s < S - 1; ++s) MOE_ISSUE(min(s, nk - 1), s);
+        wait_vm_and_barrier<(S - 2) * kDma, false>();                // barrier 0: stage 0 landed
+        int refill = S - 1;
+        for (int kt = 0; kt < nk - 1; ++kt) {
+            MOE_ISSUE(min(kt + S - 1, nk - 1), refill);             // slot of stage kt-1
+            wait_vm_and_barrier<(S - 2) * kDma, false>();            // barrier kt+1: stage kt+1 landed
+            refill = refill == S - 1 ? 0 : refill + 1;
+        }
+#undef MOE_ISSUE
+        // redundant copies may still be landing; the workgroup's LDS must be quiet first
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));           // vmcnt(0)
+        return;
     }
-    const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-        (__attribute__((address_space(3))) char*)(lds)));
-    // DMA instructions [i0, i0 + n) of stage kt into LDS slot `slot` (i0 and n are
-    // compile-time after unrolling).
-#define MOE_ISSUE(KT, SLOT, I0, NI)                                                           \
-    do {                                                                                     \
-        const uint32_t base_ = __builtin_amdgcn_readfirstlane(lds_base + (SLOT) * kStageBytes + wave * 1024); \
-        const size_t off_ = (size_t)(KT) * kRowBytes;                                        \
-        _Pragma("unroll") for (int i_ = (I0); i_ < (I0) + (NI); ++i_)                        \
-            dma16(src[i_] + off_, base_ + i_ * 4096);   /* 4 waves x 1 KiB */                \
-    } while (0)
 
-    // ---- wave layout: 2 x 2 waves, each (BT/2) tokens x (BF/2) features per operand,
-    // as TT x FT tiles of 32 x 32 (MFMA rows = features, MFMA columns = tokens) ----
+    // ---- compute: 2 x 2 waves, each (BT/2) tokens x (BF/2) features per operand, as
+    // TT x FT tiles of 32 x 32 (MFMA rows = features, MFMA columns = tokens) ----
     const int wt = wave & 1, wf = wave >> 1;
     const int l32 = lane & 31, lhalf = lane >> 5;
     const int swz = chunk_swizzle<RB>(l32);       // fragment rows start at multiples of 32
     // A tile that is not FULL (an expert's last, or only, token tile) skips the MFMAs of
     // 32-token column tiles holding no row below row_end: for an expert with a handful of
-    // rows most of the tile's MFMA work, so it runs at the speed of its weight stream.
+    // rows most of the tile's MFMA work.
     const int jn = FULL ? TT : (min(max(row_end - (row0 + wt * (BT / 2)), 0), BT / 2) + 31) / 32;
     f32x16_t acc[NB][FT][TT];
 #pragma unroll
@@ -204,12 +228,11 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[b][i][j][v] = 0.0f;
 
-    // ---- main loop: KS k-steps (16-byte chunk pairs) per stage, fragments double-
-    // buffered in registers.  Each k-step first reads the next k-step's fragments, then
-    // issues its MFMAs (scheduling barriers keep the compiler from interleaving the two),
-    // so LDS latency hides behind a block of MFMAs.  The stage barrier sits before the
-    // reads of stage kt+1: once every wave holds stage kt's last fragments, its slot is
-    // refilled with stage kt+S while stage kt+1 (landed) starts to be read. ----
+    // KS k-steps (16-byte chunk pairs) per stage, fragments double-buffered in registers.
+    // Each k-step first reads the next k-step's fragments, then issues its MFMAs
+    // (scheduling barriers keep the compiler from interleaving the two), so LDS latency
+    // hides behind a block of MFMAs.  The stage barrier sits before the reads of stage
+    // kt+1, once this wave's reads of stage kt have returned.
     uint4 fa0[TT], fw0[NB][FT], fa1[TT], fw1[NB][FT];
 #define MOE_LOAD_FRAGS(STAGE, KSTEP, FA, FW)                                                  \
     do {                                                                                     \
@@ -228,69 +251,32 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
                 _Pragma("unroll") for (int j = 0; j < TT; ++j)                               \
                     if (FULL || j < jn) Mfma<T>::mac(acc[b][i][j], FW[b][i], FA[j]);         \
     } while (0)
-    static_assert(KS % 2 == 0, "k-steps alternate between the two fragment buffers");
-
-    // The DMA for stage kt+S-1 goes into the slot stage kt-1 vacated and is interleaved
-    // with the MFMAs of stage kt, one instruction every few MFMAs: a burst of transfers
-    // can fill the memory pipeline's queue, and a wave blocked on issuing one cannot
-    // issue the MFMAs behind it.  Stage indices are clamped to the last stage, so the
-    // loop issues the same number of transfers every iteration (a redundant copy of the
-    // last stage lands in a slot no later stage reads) and every wait count is constant.
-    static_assert(kDma % KS == 0, "DMA instructions split evenly over the k-steps");
-    constexpr int kPerStep = kDma / KS;                 // DMA instructions per k-step
-    constexpr int kNm = NB * FT * TT;                   // MFMAs per k-step
-    // At the end-of-stage wait of stage kt the newest stage, kt+S-1, has issued all but
-    // its last k-step's part, so "stage kt+1 landed" allows the S-3 full stages between
-    // them plus that partial stage to remain in flight.
-    static_assert(S >= 3, "the last k-step's transfers are issued after the stage wait");
-    constexpr int kInFlight = (S - 2) * kDma - kPerStep;
-#define MOE_MFMAS_DMA(FA, FW, Q0)                                                             \
-    do {                                                                                     \
-        _Pragma("unroll") for (int b = 0; b < NB; ++b)                                       \
-            _Pragma("unroll") for (int i = 0; i < FT; ++i)                                   \
-                _Pragma("unroll") for (int j = 0; j < TT; ++j) {                             \
-            const int m_ = (b * FT + i) * TT + j;                                            \
-            if (FULL || j < jn) Mfma<T>::mac(acc[b][i][j], FW[b][i], FA[j]);                 \
-            _Pragma("unroll") for (int q_ = 0; q_ < kPerStep; ++q_) {                        \
-                if (m_ == ((q_ + 1) * kNm) / kPerStep - 1) {                                 \
-                    __builtin_amdgcn_sched_barrier(0);                                       \
-                    dma16(src[(Q0) + q_] + doff, dbase + ((Q0) + q_) * 4096);                \
-                    __builtin_amdgcn_sched_barrier(0);                                       \
-                }                                                                            \
-            }                                                                                \
-        }                                                                                    \
-    } while (0)
-    const int nk = (int)(row_bytes / kRowBytes);
-    for (int s = 0; s < S - 1; ++s) MOE_ISSUE(min(s, nk - 1), s, 0, kDma);
-    wait_vm_and_barrier<(S - 2) * kDma, false>();                 // stage 0 landed
+    __builtin_amdgcn_s_barrier();                                    // barrier 0
     MOE_LOAD_FRAGS(lds, 0, fa0, fw0);
     // The last stage is peeled off so every loop iteration has the same shape (otherwise
     // the compiler's wait insertion merges paths and drains the prefetched fragments).
-    int slot = 0, refill = S - 1;
+    int slot = 0;
     for (int kt = 0; kt < nk - 1; ++kt) {
         const char* st = lds + slot * kStageBytes;
         const int next = slot == S - 1 ? 0 : slot + 1;
-        const uint32_t dbase = __builtin_amdgcn_readfirstlane(lds_base + refill * kStageBytes + wave * 1024);
-        const size_t doff = (size_t)min(kt + S - 1, nk - 1) * kRowBytes;
 #pragma unroll
         for (int ks = 0; ks < KS; ks += 2) {
             MOE_LOAD_FRAGS(st, ks + 1, fa1, fw1);
             __builtin_amdgcn_sched_barrier(0);
-            MOE_MFMAS_DMA(fa0, fw0, ks * kPerStep);
+            MOE_MFMAS(fa0, fw0);
             __builtin_amdgcn_sched_barrier(0);
             if (ks + 2 < KS) {
                 MOE_LOAD_FRAGS(st, ks + 2, fa0, fw0);
             } else {
-                // this wave's reads of stage kt are complete; stage kt+1 landed everywhere
-                wait_vm_and_barrier<kInFlight, true>();
+                __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (3 << 14));   // lgkmcnt(0)
+                __builtin_amdgcn_s_barrier();                        // barrier kt+1
                 MOE_LOAD_FRAGS(lds + next * kStageBytes, 0, fa0, fw0);
             }
             __builtin_amdgcn_sched_barrier(0);
-            MOE_MFMAS_DMA(fa1, fw1, (ks + 1) * kPerStep);
+            MOE_MFMAS(fa1, fw1);
             __builtin_amdgcn_sched_barrier(0);
         }
         slot = next;
-        refill = refill == S - 1 ? 0 : refill + 1;
     }
     {
         const char* st = lds + slot * kStageBytes;
@@ -302,13 +288,8 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
             MOE_MFMAS(fa1, fw1);
         }
     }
-    // redundant copies of the last stage may still be landing; the workgroup's LDS must
-    // be quiet before it ends
-    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
 #undef MOE_LOAD_FRAGS
 #undef MOE_MFMAS
-#undef MOE_MFMAS_DMA
-#undef MOE_ISSUE
 
     // ---- epilogue: lane holds one token and, per 32-feature tile, 4 runs of 4 features ----
 #pragma unroll
@@ -355,7 +336,8 @@ __global__ __launch_bounds__(kThreads, 1) void dense_gemm_kernel(GemmParams<T, N
 // Grouped expert product.  XCD x (workgroups x, x + 8, ...) takes a contiguous share of
 // the tiles in dispatch order.  Tiles of one expert go in blocks of kGroupTok token tiles;
 // inside a block the feature tile varies slowest, so the ~32 tiles an XCD runs at once
-// cover about 4 token tiles x 8 feature tiles and share both operands through its L2.
+// cover about 8 token tiles x 4 feature tiles and share both operands through its L2
+// (measured best among blocks of 2 to 32 on the X-MoE Large routing).
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
 __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, NB> p) {
     __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, NB, S, RB>::kLdsBytes];
