@@ -108,6 +108,17 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
     __builtin_amdgcn_s_barrier();
 }
 
+// The same with a wave-uniform run-time count n in [LO, HI] (a compile-time wait per value).
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_and_barrier_rt(int n) {
+    if constexpr (LO >= HI) {
+        wait_vm_and_barrier<LO, false>();
+    } else {
+        if (n >= HI) wait_vm_and_barrier<HI, false>();
+        else wait_vm_and_barrier_rt<LO, HI - 1>(n);
+    }
+}
+
 // LDS layout: a stage holds BT activation rows then NB*BF weight rows, RB bytes each
 // (RB = 128: whole cache lines; RB = 64: half lines, which halves a stage so the ring can
 // be deeper), unpadded.  The 16-byte chunk c of row r sits in slot c ^ swz(r).  The LDS
@@ -189,18 +200,33 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
         // all of stage KT into slot SLOT (4 loaders x 1 KiB per 4 KiB block).  Stage indices
         // are clamped to the last stage, so every iteration issues the same transfers (a
         // redundant copy lands in a slot no later stage reads) and every wait is constant.
+        // A tile that is not FULL transfers only the activation-row blocks holding a row
+        // below row_end (the vector-memory path is limited by cache-line requests, and an
+        // expert with a handful of rows would otherwise move mostly duplicate rows).  The
+        // skipped rows' LDS holds stale data that only ever meets the MFMA columns of
+        // tokens that are never stored.
+        constexpr int kActDma = BT / kBlkRows;                         // activation blocks per loader
+        const int nact = FULL ? kActDma
+                              : min(max((min(row_end - row0, BT) - lw * kRowsPerDma + kBlkRows - 1) /
+                                            kBlkRows, 0), kActDma);
+        const int keff = kDma - (kActDma - nact);                     // transfers per slice
 #define MOE_ISSUE(KT, SLOT)                                                                   \
         do {                                                                                 \
             const uint32_t b_ = __builtin_amdgcn_readfirstlane(wbase + (SLOT) * kStageBytes); \
             const size_t o_ = (size_t)(KT) * kRowBytes;                                      \
-            _Pragma("unroll") for (int i_ = 0; i_ < kDma; ++i_) dma16(src[i_] + o_, b_ + i_ * 4096); \
+            _Pragma("unroll") for (int i_ = 0; i_ < kDma; ++i_)                              \
+                if (i_ >= kActDma || i_ < nact) dma16(src[i_] + o_, b_ + i_ * 4096);          \
         } while (0)
         for (int s = 0; s < S - 1; ++s) MOE_ISSUE(min(s, nk - 1), s);
-        wait_vm_and_barrier<(S - 2) * kDma, false>();                // barrier 0: stage 0 landed
+        // barrier 0: stage 0 landed
+        if constexpr (FULL) wait_vm_and_barrier<(S - 2) * kDma, false>();
+        else wait_vm_and_barrier_rt<(S - 2) * (kDma - kActDma), (S - 2) * kDma>((S - 2) * keff);
         int refill = S - 1;
         for (int kt = 0; kt < nk - 1; ++kt) {
             MOE_ISSUE(min(kt + S - 1, nk - 1), refill);             // slot of stage kt-1
-            wait_vm_and_barrier<(S - 2) * kDma, false>();            // barrier kt+1: stage kt+1 landed
+            // barrier kt+1: stage kt+1 landed
+            if constexpr (FULL) wait_vm_and_barrier<(S - 2) * kDma, false>();
+            else wait_vm_and_barrier_rt<(S - 2) * (kDma - kActDma), (S - 2) * kDma>((S - 2) * keff);
             refill = refill == S - 1 ? 0 : refill + 1;
         }
 #undef MOE_ISSUE
