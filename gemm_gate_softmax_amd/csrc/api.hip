@@ -49,7 +49,9 @@ moe_status_t launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
         if (st_ != MOE_OK) return st_;       \
     } while (0)
 
-size_t gate_ws(int T, int E) { return round_up((size_t)T * E * sizeof(float)); }
+size_t gate_ws(int dt, int T, int H, int E) {
+    return round_up((size_t)moe::gate_splits(dt, T, H, E) * T * E * sizeof(float));
+}
 size_t pft_ws(int T, int k, int E) { return round_up(moe::pft_ws_bytes((long long)T * k, E)); }
 size_t gemm_ws(long long N, int E) { return round_up(moe::gemm_ws_bytes(N, E)); }
 
@@ -58,13 +60,13 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 }  // namespace
 
 MOE_API size_t moe_workspace_bytes(int kind, int T, int H, int E, int F, int k, moe_dtype_t dt) {
-    (void)H; (void)F;
-    if (!valid_dt(dt) || check_route(T, E, k) != MOE_OK) return 0;
+    (void)F;
+    if (!valid_dt(dt) || check_route(T, E, k) != MOE_OK || check_dim(H) != MOE_OK) return 0;
     switch (kind) {
-        case MOE_WS_GATE: return gate_ws(T, E);
+        case MOE_WS_GATE: return gate_ws(dt, T, H, E);
         case MOE_WS_PFT: return pft_ws(T, k, E);
         case MOE_WS_GEMM: return gemm_ws((long long)T * k, E);
-        case MOE_WS_LAYER: return pft_ws(T, k, E) + gate_ws(T, E) + gemm_ws((long long)T * k, E);
+        case MOE_WS_LAYER: return pft_ws(T, k, E) + gate_ws(dt, T, H, E) + gemm_ws((long long)T * k, E);
         default: return 0;
     }
 }
@@ -90,10 +92,11 @@ MOE_API moe_status_t moe_gate_topk(moe_dtype_t dt, int T, int H, int E, int k, c
     if (T == 0) return MOE_OK;
     MOE_TRY(check_ptrs({x, wg, top_experts, top_weights, ws}));
     if (bias && !aligned16(bias)) return MOE_ERR_MISALIGNED;
-    if (ws_bytes < gate_ws(T, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    float* logits = static_cast<float*>(ws);
-    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, bias, logits, as_stream(stream))));
-    return launched(moe::launch_topk(T, E, k, logits, top_experts, top_weights, as_stream(stream)));
+    if (ws_bytes < gate_ws(dt, T, H, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    float* partials = static_cast<float*>(ws);
+    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, as_stream(stream))));
+    return launched(moe::launch_topk(T, E, k, moe::gate_splits(dt, T, H, E), partials, bias,
+                                     top_experts, top_weights, as_stream(stream)));
 }
 
 MOE_API moe_status_t moe_pft_build(int T, int k, int E, const int32_t* top_experts,
@@ -164,16 +167,17 @@ MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int 
     MOE_TRY(check_ptrs({x, wg, w1, w3, w2, out, ws, b->top_experts, b->top_weights, b->counts,
                         b->offsets, b->token_ids, b->expert_ids, b->dest_pos, b->xd, b->h, b->y}));
     if (bias && !aligned16(bias)) return MOE_ERR_MISALIGNED;
-    const size_t need_pft = pft_ws(T, k, E), need_gate = gate_ws(T, E);
+    const size_t need_pft = pft_ws(T, k, E), need_gate = gate_ws(dt, T, H, E);
     const long long N = (long long)T * k;
     if (ws_bytes < need_pft + need_gate + gemm_ws(N, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     char* w = static_cast<char*>(ws);
     void* ws_pft = w;                       // error word stays at byte 0
-    float* logits = reinterpret_cast<float*>(w + need_pft);
+    float* partials = reinterpret_cast<float*>(w + need_pft);
     void* ws_gemm = w + need_pft + need_gate;
     const hipStream_t s = as_stream(stream);
-    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, bias, logits, s)));
-    MOE_TRY(launched(moe::launch_topk(T, E, k, logits, b->top_experts, b->top_weights, s)));
+    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, s)));
+    MOE_TRY(launched(moe::launch_topk(T, E, k, moe::gate_splits(dt, T, H, E), partials, bias,
+                                      b->top_experts, b->top_weights, s)));
     MOE_TRY(launched(moe::launch_pft(T, k, E, b->top_experts, b->counts, b->offsets, b->token_ids,
                                      b->expert_ids, b->dest_pos, ws_pft, s)));
     MOE_TRY(launched(moe::launch_dispatch(dt, T, k, H, x, b->dest_pos, b->xd, s)));

@@ -25,20 +25,31 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
+// logit(t, e) = (partials[0][t][e] + partials[1][t][e] + ...) + bias[e], summed in split
+// order so the result does not depend on scheduling.
 template <int NPER>
-__global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(const float* __restrict__ logits,
-                                                                      int T, int E, int k,
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(const float* __restrict__ partials,
+                                                                      const float* __restrict__ bias,
+                                                                      int T, int E, int k, int splits,
                                                                       int32_t* __restrict__ top_experts,
                                                                       float* __restrict__ top_weights) {
     const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
     const int lane = threadIdx.x & 63;
-    const float* row = logits + (size_t)t * E;
+    const size_t stride = (size_t)T * E;
+    const float* row = partials + (size_t)t * E;
     uint64_t key[NPER];
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
         const int e = lane + kWave * i;
-        key[i] = e < E ? make_key(row[e], e) : 0ull;
+        if (e < E) {
+            float l = row[e];
+            for (int sp = 1; sp < splits; ++sp) l += row[sp * stride + e];
+            if (bias) l += bias[e];
+            key[i] = make_key(l, e);
+        } else {
+            key[i] = 0ull;
+        }
     }
     uint64_t mine = 0;  // lane j keeps pick j
     for (int j = 0; j < k; ++j) {
@@ -65,24 +76,24 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(const floa
 }
 
 template <int NPER>
-hipError_t launch_topk_n(int T, int E, int k, const float* logits, int32_t* te, float* tw,
-                         hipStream_t s) {
+hipError_t launch_topk_n(int T, int E, int k, int splits, const float* partials,
+                         const float* bias, int32_t* te, float* tw, hipStream_t s) {
     const int blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
     hipLaunchKernelGGL(topk_kernel<NPER>, dim3(blocks), dim3(kWave * kWavesPerBlock), 0, s,
-                       logits, T, E, k, te, tw);
+                       partials, bias, T, E, k, splits, te, tw);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_topk(int T, int E, int k, const float* logits, int32_t* te, float* tw,
-                       hipStream_t s) {
+hipError_t launch_topk(int T, int E, int k, int splits, const float* partials, const float* bias,
+                       int32_t* te, float* tw, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    if (E <= 64) return launch_topk_n<1>(T, E, k, logits, te, tw, s);
-    if (E <= 128) return launch_topk_n<2>(T, E, k, logits, te, tw, s);
-    if (E <= 256) return launch_topk_n<4>(T, E, k, logits, te, tw, s);
-    if (E <= 512) return launch_topk_n<8>(T, E, k, logits, te, tw, s);
-    return launch_topk_n<16>(T, E, k, logits, te, tw, s);
+    if (E <= 64) return launch_topk_n<1>(T, E, k, splits, partials, bias, te, tw, s);
+    if (E <= 128) return launch_topk_n<2>(T, E, k, splits, partials, bias, te, tw, s);
+    if (E <= 256) return launch_topk_n<4>(T, E, k, splits, partials, bias, te, tw, s);
+    if (E <= 512) return launch_topk_n<8>(T, E, k, splits, partials, bias, te, tw, s);
+    return launch_topk_n<16>(T, E, k, splits, partials, bias, te, tw, s);
 }
 
 }  // namespace moe

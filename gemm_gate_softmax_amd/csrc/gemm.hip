@@ -57,7 +57,7 @@ struct GemmParams {
     const int* table_count; // entries in table
     int dense_rows;         // rows of the single expert of a dense product (gate)
     void* out;              // [rows][n_feat]: fp32 logits or storage type
-    const float* bias;      // logits epilogue only (nullable)
+    int k_slices;           // dense product: k-slices per K split (0: the whole K)
 };
 
 // Writes 4 consecutive features of one token: fp32 logits (+ bias, per-element bounds),
@@ -69,7 +69,7 @@ __device__ __forceinline__ void store_run(const GemmParams<T, NB>& p, int tok, i
         float* o = reinterpret_cast<float*>(p.out) + (size_t)tok * p.n_feat;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            if (feat + v < p.n_feat) o[feat + v] = r[v] + (p.bias ? p.bias[feat + v] : 0.0f);
+            if (feat + v < p.n_feat) o[feat + v] = r[v];
     } else if constexpr (sizeof(T) == 4) {
         if (feat >= p.n_feat) return;
         float* o = reinterpret_cast<float*>(p.out) + (size_t)tok * p.n_feat + feat;
@@ -153,7 +153,7 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
 // read while stage kt+S-1 is loaded into the slot stage kt-1 left.
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool FULL>
 __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* lds, int expert,
-                                             int row0, int row_end, int f0) {
+                                             int row0, int row_end, int f0, int s0, int nk) {
     using Tile = CompTile<BT, BF, NB, S, RB>;
     constexpr int kRowBytes = Tile::kRowBytes;
     constexpr int kRowsPerDma = 1024 / kRowBytes;    // rows per 1 KiB DMA instruction
@@ -171,7 +171,7 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const size_t row_bytes = (size_t)p.K * sizeof(T);
-    const int nk = (int)(row_bytes / kRowBytes);
+    const size_t k_off = (size_t)s0 * kRowBytes;     // first k-slice of this tile's K range
 
     if (wave >= 4) {
         // ---- loader: wave 4 + w fills row blocks w + 4 i of every stage.  Block b <
@@ -187,12 +187,12 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
             const int c = (lane % kChunks) ^ chunk_swizzle<RB>(r);    // chunk held by this slot
             if (i < BT / kBlkRows) {
                 const int ar = min(row0 + r, p.act_rows - 1);
-                src[i] = reinterpret_cast<const char*>(p.act) + (size_t)ar * row_bytes + c * 16;
+                src[i] = reinterpret_cast<const char*>(p.act) + (size_t)ar * row_bytes + k_off + c * 16;
             } else {
                 const int b = (kBlkRows * i - BT) / BF;
                 const int f = min(f0 + (r - BT) - b * BF, p.n_feat - 1);
                 src[i] = reinterpret_cast<const char*>(p.w[b] + (size_t)expert * p.w_stride) +
-                         (size_t)f * row_bytes + c * 16;
+                         (size_t)f * row_bytes + k_off + c * 16;
             }
         }
         const uint32_t wbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
@@ -344,19 +344,28 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
 __global__ __launch_bounds__(kThreads, 1) void dense_gemm_kernel(GemmParams<T, NB> p) {
     __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, NB, S, RB>::kLdsBytes];
+    // work item L = (split, token tile, feature tile), feature tile fastest so the
+    // workgroups an XCD runs at once share their activation rows through its L2
     const int ntt = (p.dense_rows + BT - 1) / BT;
-    const int total = ntt * p.feat_tiles;
+    const int nk_all = (int)((size_t)p.K * sizeof(T) / RB);
+    const int splits = (nk_all + p.k_slices - 1) / p.k_slices;
+    const int tiles = ntt * p.feat_tiles;
+    const int total = tiles * splits;
     const int chunk = (total + 7) >> 3;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
     if (local >= chunk) return;
     const int L = xcd * chunk + local;
     if (L >= total) return;
-    const int ftile = L / ntt, ttile = L - ftile * ntt;
+    const int split = L / tiles, rem = L - split * tiles;
+    const int ttile = rem / p.feat_tiles, ftile = rem - ttile * p.feat_tiles;
+    const int s0 = split * p.k_slices, nk = min(p.k_slices, nk_all - s0);
+    GemmParams<T, NB> q = p;
+    q.out = static_cast<float*>(p.out) + (size_t)split * p.dense_rows * p.n_feat;
     const int row_end = min(p.dense_rows, p.act_rows);
     if (row_end - ttile * BT >= BT)
-        compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, 0, ttile * BT, row_end, ftile * BF);
+        compute_tile<T, NB, EPI, BT, BF, S, RB, true>(q, lds, 0, ttile * BT, row_end, ftile * BF, s0, nk);
     else
-        compute_tile<T, NB, EPI, BT, BF, S, RB, false>(p, lds, 0, ttile * BT, row_end, ftile * BF);
+        compute_tile<T, NB, EPI, BT, BF, S, RB, false>(q, lds, 0, ttile * BT, row_end, ftile * BF, s0, nk);
 }
 
 // Grouped expert product.  XCD x (workgroups x, x + 8, ...) takes a contiguous share of
@@ -384,10 +393,11 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, 
     const int ftile = ql / width;
     const int ttile = blk * kGroupTok + (ql - ftile * width);
     const int row0 = seg0 + ttile * BT, row_end = min(seg0 + segn, p.act_rows);
+    const int nk = (int)((size_t)p.K * sizeof(T) / RB);
     if (row_end - row0 >= BT)
-        compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, expert, row0, row_end, ftile * BF);
+        compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, expert, row0, row_end, ftile * BF, 0, nk);
     else
-        compute_tile<T, NB, EPI, BT, BF, S, RB, false>(p, lds, expert, row0, row_end, ftile * BF);
+        compute_tile<T, NB, EPI, BT, BF, S, RB, false>(p, lds, expert, row0, row_end, ftile * BF, 0, nk);
 }
 
 // Tile table, built on the device from the offsets (no host read of the counts): one
@@ -437,10 +447,23 @@ hipError_t launch_expert(const GemmParams<T, NB>& p, int max_tiles, hipStream_t 
     return hipGetLastError();
 }
 
+// Gate logits as kGateSplits-free K splits: enough (token tile, expert tile, K split) work
+// items to give every CU about four, each split's fp32 partial sums [T][E] written to its
+// own slice of `partials`; the top-k kernel adds them in split order and adds the bias.
+constexpr int kGateBT = 64, kGateBF = 64, kGateStages = 4, kGateRB = 128;
+
+__host__ __device__ inline int gate_k_slices(int dt, int T, int H, int E) {
+    const int nk = H * (dt == 0 ? 4 : 2) / kGateRB;
+    const int tiles = ((T + kGateBT - 1) / kGateBT) * ((E + kGateBF - 1) / kGateBF);
+    int splits = 1024 / (tiles > 0 ? tiles : 1);
+    splits = splits < 1 ? 1 : (splits > 8 ? 8 : splits);
+    splits = splits > nk ? nk : splits;
+    return (nk + splits - 1) / splits;              // k-slices per split
+}
+
 template <typename T>
-hipError_t gate_logits_t(int T_, int H, int E, const void* x, const void* wg, const float* bias,
-                         float* logits, hipStream_t s) {
-    constexpr int BT = 64, BF = 64, S = 4;
+hipError_t gate_logits_t(int dt, int T_, int H, int E, const void* x, const void* wg,
+                         float* partials, hipStream_t s) {
     GemmParams<T, 1> p{};
     p.act = static_cast<const T*>(x);
     p.act_rows = T_;
@@ -448,12 +471,14 @@ hipError_t gate_logits_t(int T_, int H, int E, const void* x, const void* wg, co
     p.w[0] = static_cast<const T*>(wg);
     p.w_stride = 0;
     p.n_feat = E;
-    p.feat_tiles = (E + BF - 1) / BF;
+    p.feat_tiles = (E + kGateBF - 1) / kGateBF;
     p.dense_rows = T_;
-    p.out = logits;
-    p.bias = bias;
-    const int grid = ((T_ + BT - 1) / BT) * p.feat_tiles;
-    return launch_dense<T, 1, kEpiLogits, BT, BF, S, 128>(p, grid, s);
+    p.out = partials;
+    p.k_slices = gate_k_slices(dt, T_, H, E);
+    const int nk = H * (int)sizeof(T) / kGateRB;
+    const int splits = (nk + p.k_slices - 1) / p.k_slices;
+    const int grid = ((T_ + kGateBT - 1) / kGateBT) * p.feat_tiles * splits;
+    return launch_dense<T, 1, kEpiLogits, kGateBT, kGateBF, kGateStages, kGateRB>(p, grid, s);
 }
 
 struct TableLayout {
@@ -525,11 +550,17 @@ size_t gemm_ws_bytes(long long N, int E) {
     return 256 + (size_t)tiles_cap(N, E) * sizeof(int4);
 }
 
+int gate_splits(int dt, int T, int H, int E) {
+    const int nk = H * (dt == 0 ? 4 : 2) / kGateRB;
+    const int per = gate_k_slices(dt, T, H, E);
+    return (nk + per - 1) / per;
+}
+
 hipError_t launch_gate_logits(int dt, int T, int H, int E, const void* x, const void* wg,
-                              const float* bias, float* logits, hipStream_t s) {
+                              float* partials, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    return dt == 0 ? gate_logits_t<float>(T, H, E, x, wg, bias, logits, s)
-                   : gate_logits_t<bf16_t>(T, H, E, x, wg, bias, logits, s);
+    return dt == 0 ? gate_logits_t<float>(dt, T, H, E, x, wg, partials, s)
+                   : gate_logits_t<bf16_t>(dt, T, H, E, x, wg, partials, s);
 }
 
 hipError_t launch_grouped_gemm(int dt, int N, int E, int H, int F, const void* xd,

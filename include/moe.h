@@ -61,8 +61,9 @@ typedef enum {
     MOE_WS_LAYER = 3
 } moe_workspace_kind_t;
 
-/* Bytes of workspace a call needs for these sizes (0 for unsupported arguments).  Sizes
- * that do not matter to a call are ignored (e.g. H and F for MOE_WS_PFT). */
+/* Bytes of workspace a call needs for these sizes (0 for unsupported arguments, including
+ * H not a positive multiple of 64).  Sizes that do not matter to a call are ignored (e.g.
+ * F for MOE_WS_PFT). */
 size_t moe_workspace_bytes(int kind, int T, int H, int E, int F, int k, moe_dtype_t dt);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -76,7 +77,9 @@ const char *moe_status_string(moe_status_t status);
  *   top_weights[t][j]  = softmax(logit[t])[pick j] renormalised over the k picks
  *                      = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)
  * bias may be NULL (no bias).  Outputs: top_experts [T][k] int32, top_weights [T][k] fp32.
- * ws: moe_workspace_bytes(MOE_WS_GATE, ...) bytes (holds the fp32 logits).
+ * ws: moe_workspace_bytes(MOE_WS_GATE, ...) bytes (depends on T, H, E and dt: it holds
+ * fp32 partial logits over up to 8 splits of the hidden dimension, which the top-k step
+ * adds in split order before the bias).
  */
 moe_status_t moe_gate_topk(moe_dtype_t dt, int T, int H, int E, int k, const void *x,
                            const void *wg, const float *bias, int32_t *top_experts,
