@@ -165,7 +165,8 @@ MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int 
     MOE_TRY(check_dim(F));
     if (T == 0) return MOE_OK;
     MOE_TRY(check_ptrs({x, wg, w1, w3, w2, out, ws, b->top_experts, b->top_weights, b->counts,
-                        b->offsets, b->token_ids, b->expert_ids, b->dest_pos, b->xd, b->h, b->y}));
+                        b->offsets, b->token_ids, b->expert_ids, b->dest_pos, b->h, b->y}));
+    if (b->xd && !aligned16(b->xd)) return MOE_ERR_MISALIGNED;
     if (bias && !aligned16(bias)) return MOE_ERR_MISALIGNED;
     const size_t need_pft = pft_ws(T, k, E), need_gate = gate_ws(dt, T, H, E);
     const long long N = (long long)T * k;
@@ -180,8 +181,14 @@ MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int 
                                       b->top_experts, b->top_weights, s)));
     MOE_TRY(launched(moe::launch_pft(T, k, E, b->top_experts, b->counts, b->offsets, b->token_ids,
                                      b->expert_ids, b->dest_pos, ws_pft, s)));
-    MOE_TRY(launched(moe::launch_dispatch(dt, T, k, H, x, b->dest_pos, b->xd, s)));
-    MOE_TRY(launched(moe::launch_grouped_gemm(dt, (int)N, E, H, F, b->xd, b->offsets, w1, w3, w2,
-                                              b->h, b->y, ws_gemm, s)));
+    if (b->xd) {
+        MOE_TRY(launched(moe::launch_dispatch(dt, T, k, H, x, b->dest_pos, b->xd, s)));
+        MOE_TRY(launched(moe::launch_grouped_gemm(dt, (int)N, E, H, F, b->xd, b->offsets, w1, w3,
+                                                  w2, b->h, b->y, ws_gemm, s)));
+    } else {  // dispatch fused into the expert product: rows gathered from x on load
+        MOE_TRY(launched(moe::launch_grouped_gemm_gather(dt, (int)N, E, H, F, x, T, b->token_ids,
+                                                         b->offsets, w1, w3, w2, b->h, b->y,
+                                                         ws_gemm, s)));
+    }
     return launched(moe::launch_combine(dt, T, k, H, b->y, b->dest_pos, b->top_weights, out, s));
 }

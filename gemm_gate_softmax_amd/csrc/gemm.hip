@@ -46,8 +46,10 @@ constexpr int kGroupTok = MOE_GROUP_TOK;      // token tiles per L2-sharing bloc
 
 template <typename T, int NB>
 struct GemmParams {
-    const T* act;           // activation rows [act_rows][K]
-    int act_rows;           // rows addressable in act (loads are clamped below it)
+    const T* act;           // activation rows [act_rows][K], or [src_rows][K] when gathered
+    int act_rows;           // rows of the product (loads are clamped below it)
+    const int32_t* gather;  // nullable: product row r reads act row gather[r] (< src_rows)
+    int src_rows;           // rows of act when gathered
     int K;                  // shared dimension, elements
     const T* w[NB];         // weight operands; expert e starts at w[b] + e * w_stride
     long long w_stride;     // elements per expert
@@ -186,7 +188,8 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
             const int r = (lw + 4 * i) * kRowsPerDma + rl;            // row within the stage
             const int c = (lane % kChunks) ^ chunk_swizzle<RB>(r);    // chunk held by this slot
             if (i < BT / kBlkRows) {
-                const int ar = min(row0 + r, p.act_rows - 1);
+                int ar = min(row0 + r, p.act_rows - 1);
+                if (p.gather) ar = min(max(p.gather[ar], 0), p.src_rows - 1);   // fused dispatch
                 src[i] = reinterpret_cast<const char*>(p.act) + (size_t)ar * row_bytes + k_off + c * 16;
             } else {
                 const int b = (kBlkRows * i - BT) / BF;
@@ -501,9 +504,9 @@ inline TableLayout carve_tables(void* ws, int N, int E) {
 }
 
 template <typename T>
-hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* offsets,
-                     const void* w1, const void* w3, const void* w2, void* h, void* y, void* ws,
-                     hipStream_t s) {
+hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* gather,
+                     int src_rows, const int32_t* offsets, const void* w1, const void* w3,
+                     const void* w2, void* h, void* y, void* ws, hipStream_t s) {
     constexpr int BT = kExpertBTok;
     const TableLayout tl = carve_tables(ws, N, E);
     hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, N, BT, tl.cap,
@@ -516,6 +519,8 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
     GemmParams<T, 2> up{};
     up.act = static_cast<const T*>(xd);
     up.act_rows = N;
+    up.gather = gather;
+    up.src_rows = src_rows;
     up.K = H;
     up.w[0] = static_cast<const T*>(w1);
     up.w[1] = static_cast<const T*>(w3);
@@ -567,8 +572,17 @@ hipError_t launch_grouped_gemm(int dt, int N, int E, int H, int F, const void* x
                                const int32_t* offsets, const void* w1, const void* w3,
                                const void* w2, void* h, void* y, void* ws, hipStream_t s) {
     if (N == 0) return hipSuccess;
-    return dt == 0 ? grouped_t<float>(N, E, H, F, xd, offsets, w1, w3, w2, h, y, ws, s)
-                   : grouped_t<bf16_t>(N, E, H, F, xd, offsets, w1, w3, w2, h, y, ws, s);
+    return dt == 0 ? grouped_t<float>(N, E, H, F, xd, nullptr, 0, offsets, w1, w3, w2, h, y, ws, s)
+                   : grouped_t<bf16_t>(N, E, H, F, xd, nullptr, 0, offsets, w1, w3, w2, h, y, ws, s);
+}
+
+hipError_t launch_grouped_gemm_gather(int dt, int N, int E, int H, int F, const void* x, int T,
+                                      const int32_t* token_ids, const int32_t* offsets,
+                                      const void* w1, const void* w3, const void* w2, void* h,
+                                      void* y, void* ws, hipStream_t s) {
+    if (N == 0) return hipSuccess;
+    return dt == 0 ? grouped_t<float>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, ws, s)
+                   : grouped_t<bf16_t>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, ws, s);
 }
 
 }  // namespace moe

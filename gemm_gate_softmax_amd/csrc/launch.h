@@ -33,5 +33,11 @@ size_t gemm_ws_bytes(long long N, int E);
 hipError_t launch_grouped_gemm(int dt, int N, int E, int H, int F, const void* xd,
                                const int32_t* offsets, const void* w1, const void* w3,
                                const void* w2, void* h, void* y, void* ws, hipStream_t s);
+// The same product with the dispatch fused in: row p of the up product reads x[token_ids[p]]
+// (x has T rows) instead of xd[p]; nothing is written for xd.
+hipError_t launch_grouped_gemm_gather(int dt, int N, int E, int H, int F, const void* x, int T,
+                                      const int32_t* token_ids, const int32_t* offsets,
+                                      const void* w1, const void* w3, const void* w2, void* h,
+                                      void* y, void* ws, hipStream_t s);
 
 }  // namespace moe

@@ -221,7 +221,9 @@ def moe_combine(y, dest_pos, top_weights, out=None, stream=None):
     return out
 
 
-def alloc_layer_bufs(T, H, E, F, k, dtype, device) -> dict:
+def alloc_layer_bufs(T, H, E, F, k, dtype, device, fuse_dispatch=False) -> dict:
+    """Intermediates of moe_layer_forward.  fuse_dispatch=True leaves xd out (None): the
+    layer then gathers the expert rows from x on load and never writes xd."""
     N = T * k
     i32 = dict(dtype=torch.int32, device=device)
     return dict(top_experts=torch.empty((T, k), **i32),
@@ -229,13 +231,15 @@ def alloc_layer_bufs(T, H, E, F, k, dtype, device) -> dict:
                 counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
                 token_ids=torch.empty(N, **i32), expert_ids=torch.empty(N, **i32),
                 dest_pos=torch.empty((T, k), **i32),
-                xd=torch.empty((N, H), dtype=dtype, device=device),
+                xd=None if fuse_dispatch else torch.empty((N, H), dtype=dtype, device=device),
                 h=torch.empty((N, F), dtype=dtype, device=device),
                 y=torch.empty((N, H), dtype=dtype, device=device))
 
 
-def moe_layer_forward(x, wg, bias, w1, w3, w2, k, out=None, bufs=None, ws=None, stream=None):
-    """Whole layer.  Returns (out [T,H], bufs dict of intermediates, ws)."""
+def moe_layer_forward(x, wg, bias, w1, w3, w2, k, out=None, bufs=None, ws=None, stream=None,
+                      fuse_dispatch=False):
+    """Whole layer.  Returns (out [T,H], bufs dict of intermediates, ws).  With
+    fuse_dispatch (or bufs["xd"] None) the dispatch is fused into the expert product."""
     dt = dtype_code(x.dtype)
     T, H = x.shape
     E, F = w1.shape[0], w1.shape[1]
@@ -246,7 +250,8 @@ def moe_layer_forward(x, wg, bias, w1, w3, w2, k, out=None, bufs=None, ws=None, 
         _need(bias, "bias", torch.float32, (E,))
     out = torch.empty((T, H), dtype=x.dtype, device=x.device) if out is None else out
     _need(out, "out", x.dtype, (T, H))
-    bufs = alloc_layer_bufs(T, H, E, F, k, x.dtype, x.device) if bufs is None else bufs
+    if bufs is None:
+        bufs = alloc_layer_bufs(T, H, E, F, k, x.dtype, x.device, fuse_dispatch)
     ws = workspace(MOE_WS_LAYER, T, H, E, F, k, dt, x.device) if ws is None else ws
     cb = LayerBufs(*[_ptr(bufs[n]) for n, _ in LayerBufs._fields_])
     _check("moe_layer_forward", lib().moe_layer_forward(

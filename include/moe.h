@@ -151,7 +151,7 @@ typedef struct moe_layer_bufs {
     int32_t *token_ids;   /* [N]    */
     int32_t *expert_ids;  /* [N]    */
     int32_t *dest_pos;    /* [T][k] */
-    void *xd;             /* [N][H] */
+    void *xd;             /* [N][H], or NULL (dispatch fused into the experts) */
     void *h;              /* [N][F] */
     void *y;              /* [N][H] */
 } moe_layer_bufs;
@@ -160,7 +160,9 @@ typedef struct moe_layer_bufs {
  * The whole layer forward: gate -> buffers -> dispatch -> experts -> combine, each stage
  * exactly as the entry point of the same name, enqueued back to back on `stream` with no
  * host synchronisation.  x [T][H] -> out [T][H]; intermediates land in *bufs (every
- * pointer required).  ws: moe_workspace_bytes(MOE_WS_LAYER, ...) bytes; its byte-0 int32
+ * pointer required except xd).  bufs->xd NULL fuses the dispatch into the expert product
+ * (rows gathered from x through token_ids as they are loaded, the next step the X-MoE
+ * review's padding-free dispatch allows): xd is not written and the results are identical.  ws: moe_workspace_bytes(MOE_WS_LAYER, ...) bytes; its byte-0 int32
  * is the error word of moe_pft_build.
  */
 moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k,

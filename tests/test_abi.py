@@ -130,4 +130,8 @@ def test_gemm_and_layer_reject(L):
     assert lf(*args(bufs=nb)) == INVALID
     mb = ops.LayerBufs(*([A] * 8 + [MIS, A]))
     assert lf(*args(bufs=mb)) == MISALIGNED
+    xb = ops.LayerBufs(*([A] * 7 + [MIS, A, A]))        # xd may be NULL, never misaligned
+    assert lf(*args(bufs=xb)) == MISALIGNED
+    nb7 = ops.LayerBufs(*([A] * 6 + [None, None, A, A]))  # dest_pos stays required
+    assert lf(*args(bufs=nb7)) == INVALID
     assert lf(*args(T=0)) == OK

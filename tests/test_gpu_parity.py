@@ -237,6 +237,26 @@ def test_layer_deterministic():
     assert torch.equal(a, b)
 
 
+FUSED_CASES = SMALL_LAYERS + [W.CONFIGS["xmoe_small"], W.CONFIGS["xmoe_large"]]
+
+
+@pytest.mark.parametrize("cfg", FUSED_CASES, ids=lambda c: c.name)
+def test_layer_fused_dispatch_identical(orc, cfg):
+    # bufs.xd = NULL gathers the expert rows from x through token_ids on load: the same
+    # values reach the same MFMAs in the same order, so every output is bit-identical to
+    # the staged path, and the oracle pins the staged path elsewhere.
+    d = W.make_device(cfg, seed=2, device=DEV)
+    args = (d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k)
+    out_s, b_s, _ = ops.moe_layer_forward(*args)
+    out_f, b_f, _ = ops.moe_layer_forward(*args, fuse_dispatch=True)
+    torch.cuda.synchronize()
+    assert b_f["xd"] is None
+    for n in ("top_experts", "counts", "offsets", "token_ids", "dest_pos", "h", "y"):
+        assert torch.equal(b_s[n], b_f[n]), n
+    assert torch.equal(out_s, out_f)
+    _log(f"[fused] {cfg.name}: staged and fused-dispatch layers agree bit for bit")
+
+
 def test_layer_zero_tokens():
     cfg = SMALL_LAYERS[0].scaled(T=0)
     d = W.make_device(cfg, seed=0, device=DEV)
