@@ -12,6 +12,8 @@ per-stage table goes to stderr first.
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config xmoe_large]
                   [--no-cpu-baseline] [--cpu-seconds 15]
   python bench.py --calibrate-copy     # plain 1 GiB device copies, for HBM byte counters
+  python bench.py --up-kernel-only     # one staged layer, then only the up-product calls
+                                       # (the launches the traffic counters are read on)
 
 The roofline object covers the dominant kernel, the expert gate/up product with its
 SwiGLU epilogue (two thirds of the layer's flops), timed on its own through the same
@@ -61,6 +63,8 @@ def parse():
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain device copies of 1 GiB (counter calibration)")
+    ap.add_argument("--up-kernel-only", action="store_true",
+                    help="one staged layer, then --steps calls of the up product alone")
     return ap.parse_args()
 
 
@@ -198,6 +202,18 @@ def main():
     ws = ops.workspace(ops.MOE_WS_LAYER, cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, dtc, dev)
     out = torch.empty_like(d["x"])
     stream = torch.cuda.current_stream()
+
+    if args.up_kernel_only:
+        step_staged_once = lambda: ops.moe_layer_forward(
+            d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k, out=out, bufs=bufs, ws=ws)
+        step_staged_once()
+        gws0 = ops.workspace(ops.MOE_WS_GEMM, cfg.N, cfg.H, cfg.E, cfg.F, 1, dtc, dev)
+        for _ in range(args.steps):
+            ops.moe_grouped_gemm_swiglu(bufs["xd"], bufs["offsets"], d["w1"], d["w3"], None,
+                                        h=bufs["h"], ws=gws0)
+        torch.cuda.synchronize()
+        print(json.dumps({"up_kernel_only": args.steps, "workload": cfg.name}), flush=True)
+        return 0
 
     def step():          # the layer with the dispatch fused into the up product
         ops.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k,

@@ -1,7 +1,11 @@
 """Summaries of rocprofv3 CSV output for this library's kernels (text for profiles/).
 
   python -m gemm_gate_softmax_amd.profile_summary stats KERNEL_STATS.csv --command "..."
-      Markdown table of a ``rocprofv3 --kernel-trace --stats --output-format csv`` run.
+        [--trace KERNEL_TRACE.csv --kernel PREFIX --last N]
+      Markdown table of a ``rocprofv3 --kernel-trace --stats --output-format csv`` run; with
+      --trace, also the mean duration of the last N dispatches of the kernel named PREFIX
+      (e.g. the calls a benchmark times last, when earlier calls of the same kernel ran
+      with other arguments).
 
   python -m gemm_gate_softmax_amd.profile_summary traffic --kernel PREFIX --workload NAME \\
       --fetch BENCH_FETCH.csv --write BENCH_WRITE.csv \\
@@ -46,7 +50,14 @@ def kernel_digest():
     return h.hexdigest()[:16]
 
 
-def stats_markdown(path, command, title):
+def last_dispatches(trace, prefix, n):
+    """Durations (us) of the last n dispatches of kernels whose name contains prefix."""
+    rows = [r for r in _rows(trace) if prefix in _short(r["Kernel_Name"], 10**6)]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[-n:]]
+
+
+def stats_markdown(path, command, title, trace=None, prefix=None, last=0):
     rows = sorted(_rows(path), key=lambda r: -float(r["TotalDurationNs"]))
     out = [f"# {title}", "", "Command (repository root, one MI355X):", "", f"    {command}", "",
            "`Calls` counts dispatches over the whole run (warm-up, timed steps, per-stage",
@@ -57,6 +68,11 @@ def stats_markdown(path, command, title):
         out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                    f"{float(r['Percentage']):.2f} |")
+    if trace and prefix and last > 0:
+        d = last_dispatches(trace, prefix, last)
+        out += ["", f"Last {len(d)} dispatches of `{prefix}` (the calls the benchmark times "
+                "last, from the kernel trace of the same run): mean "
+                f"{statistics.mean(d):.1f} us, min {min(d):.1f}, max {max(d):.1f}."]
     return "\n".join(out) + "\n"
 
 
@@ -121,14 +137,17 @@ def main(argv=None):
     s.add_argument("csv")
     s.add_argument("--command", required=True)
     s.add_argument("--title", default="rocprofv3 kernel summary")
+    s.add_argument("--trace")
+    s.add_argument("--kernel")
+    s.add_argument("--last", type=int, default=0)
     t = sub.add_parser("traffic")
     for k in ("kernel", "workload", "fetch", "write", "copy_fetch", "copy_write"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--command", action="append", required=True)
     a = ap.parse_args(argv)
-    sys.stdout.write(stats_markdown(a.csv, a.command, a.title) if a.cmd == "stats"
-                     else traffic_markdown(a))
+    sys.stdout.write(stats_markdown(a.csv, a.command, a.title, a.trace, a.kernel, a.last)
+                     if a.cmd == "stats" else traffic_markdown(a))
     return 0
 
 
