@@ -41,6 +41,8 @@ moe_status_t check_ptrs(std::initializer_list<const void*> ps) {
     return MOE_OK;
 }
 
+bool valid_routing(moe_routing_t r) { return r == MOE_ROUTE_SOFTMAX || r == MOE_ROUTE_SIGMOID; }
+
 moe_status_t launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
 #define MOE_TRY(expr)                        \
@@ -83,10 +85,11 @@ MOE_API const char* moe_status_string(moe_status_t s) {
     }
 }
 
-MOE_API moe_status_t moe_gate_topk(moe_dtype_t dt, int T, int H, int E, int k, const void* x,
+MOE_API moe_status_t moe_gate_topk(moe_dtype_t dt, int T, int H, int E, int k,
+                                   moe_routing_t routing, const void* x,
                                    const void* wg, const float* bias, int32_t* top_experts,
                                    float* top_weights, void* ws, size_t ws_bytes, void* stream) {
-    if (!valid_dt(dt)) return MOE_ERR_INVALID_VALUE;
+    if (!valid_dt(dt) || !valid_routing(routing)) return MOE_ERR_INVALID_VALUE;
     MOE_TRY(check_route(T, E, k));
     MOE_TRY(check_dim(H));
     if (T == 0) return MOE_OK;
@@ -95,8 +98,8 @@ MOE_API moe_status_t moe_gate_topk(moe_dtype_t dt, int T, int H, int E, int k, c
     if (ws_bytes < gate_ws(dt, T, H, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     float* partials = static_cast<float*>(ws);
     MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, as_stream(stream))));
-    return launched(moe::launch_topk(T, E, k, moe::gate_splits(dt, T, H, E), partials, bias,
-                                     top_experts, top_weights, as_stream(stream)));
+    return launched(moe::launch_topk(T, E, k, routing, moe::gate_splits(dt, T, H, E), partials,
+                                     bias, top_experts, top_weights, as_stream(stream)));
 }
 
 MOE_API moe_status_t moe_pft_build(int T, int k, int E, const int32_t* top_experts,
@@ -155,11 +158,12 @@ MOE_API moe_status_t moe_combine(moe_dtype_t dt, int T, int k, int H, const void
 }
 
 MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k,
-                                       const void* x, const void* wg, const float* bias,
-                                       const void* w1, const void* w3, const void* w2,
+                                       moe_routing_t routing, const void* x, const void* wg,
+                                       const float* bias, const void* w1, const void* w3,
+                                       const void* w2,
                                        void* out, const moe_layer_bufs* b, void* ws,
                                        size_t ws_bytes, void* stream) {
-    if (!valid_dt(dt) || !b) return MOE_ERR_INVALID_VALUE;
+    if (!valid_dt(dt) || !valid_routing(routing) || !b) return MOE_ERR_INVALID_VALUE;
     MOE_TRY(check_route(T, E, k));
     MOE_TRY(check_dim(H));
     MOE_TRY(check_dim(F));
@@ -177,8 +181,8 @@ MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int 
     void* ws_gemm = w + need_pft + need_gate;
     const hipStream_t s = as_stream(stream);
     MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, s)));
-    MOE_TRY(launched(moe::launch_topk(T, E, k, moe::gate_splits(dt, T, H, E), partials, bias,
-                                      b->top_experts, b->top_weights, s)));
+    MOE_TRY(launched(moe::launch_topk(T, E, k, routing, moe::gate_splits(dt, T, H, E), partials,
+                                      bias, b->top_experts, b->top_weights, s)));
     MOE_TRY(launched(moe::launch_pft(T, k, E, b->top_experts, b->counts, b->offsets, b->token_ids,
                                      b->expert_ids, b->dest_pos, ws_pft, s)));
     if (b->xd) {

@@ -1,11 +1,12 @@
 // gate.hip -- top-k selection and renormalised softmax weights, one wave64 per token.
 //
 // Gating as in the X-MoE review (section 三, 训练流程 step 2: the gate emits the routing in
-// buffer form, no dense dispatch mask) with softmax top-k routing (FSMoE report, 第六部分
-// lists the routing functions a layer may use).  Selection orders experts by (logit desc,
-// expert id asc); the weights are softmax over all E logits renormalised over the k picks,
+// buffer form, no dense dispatch mask) with top-k routing (FSMoE report, 第六部分 lists the
+// routing functions a layer may use, softmax and sigmoid among them).  Selection orders
+// experts by (logit desc, expert id asc) for both, since both scores increase with the
+// logit.  Softmax weights are softmax over all E logits renormalised over the k picks,
 // which equals exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0) because the full denominator
-// cancels.
+// cancels; sigmoid weights are s_j / sum_{i<k} s_i with s = 1 / (1 + exp(-l)).
 #include "device.h"
 #include "launch.h"
 
@@ -27,7 +28,7 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
 
 // logit(t, e) = (partials[0][t][e] + partials[1][t][e] + ...) + bias[e], summed in split
 // order so the result does not depend on scheduling.
-template <int NPER>
+template <int NPER, int ROUTE>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(const float* __restrict__ partials,
                                                                       const float* __restrict__ bias,
                                                                       int T, int E, int k, int splits,
@@ -67,7 +68,8 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(const floa
     }
     const float lj = key_logit(mine);
     const float l0 = __shfl(lj, 0, kWave);
-    const float ex = lane < k ? expf(lj - l0) : 0.0f;
+    float ex = 0.0f;
+    if (lane < k) ex = ROUTE == 0 ? expf(lj - l0) : 1.0f / (1.0f + expf(-lj));
     const float z = wave_sum_f32(ex);
     if (lane < k) {
         top_experts[(size_t)t * k + lane] = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(mine));
@@ -76,24 +78,28 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(const floa
 }
 
 template <int NPER>
-hipError_t launch_topk_n(int T, int E, int k, int splits, const float* partials,
+hipError_t launch_topk_n(int T, int E, int k, int routing, int splits, const float* partials,
                          const float* bias, int32_t* te, float* tw, hipStream_t s) {
     const int blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL(topk_kernel<NPER>, dim3(blocks), dim3(kWave * kWavesPerBlock), 0, s,
-                       partials, bias, T, E, k, splits, te, tw);
+    if (routing == 0)
+        hipLaunchKernelGGL((topk_kernel<NPER, 0>), dim3(blocks), dim3(kWave * kWavesPerBlock), 0, s,
+                           partials, bias, T, E, k, splits, te, tw);
+    else
+        hipLaunchKernelGGL((topk_kernel<NPER, 1>), dim3(blocks), dim3(kWave * kWavesPerBlock), 0, s,
+                           partials, bias, T, E, k, splits, te, tw);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_topk(int T, int E, int k, int splits, const float* partials, const float* bias,
-                       int32_t* te, float* tw, hipStream_t s) {
+hipError_t launch_topk(int T, int E, int k, int routing, int splits, const float* partials,
+                       const float* bias, int32_t* te, float* tw, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    if (E <= 64) return launch_topk_n<1>(T, E, k, splits, partials, bias, te, tw, s);
-    if (E <= 128) return launch_topk_n<2>(T, E, k, splits, partials, bias, te, tw, s);
-    if (E <= 256) return launch_topk_n<4>(T, E, k, splits, partials, bias, te, tw, s);
-    if (E <= 512) return launch_topk_n<8>(T, E, k, splits, partials, bias, te, tw, s);
-    return launch_topk_n<16>(T, E, k, splits, partials, bias, te, tw, s);
+    if (E <= 64) return launch_topk_n<1>(T, E, k, routing, splits, partials, bias, te, tw, s);
+    if (E <= 128) return launch_topk_n<2>(T, E, k, routing, splits, partials, bias, te, tw, s);
+    if (E <= 256) return launch_topk_n<4>(T, E, k, routing, splits, partials, bias, te, tw, s);
+    if (E <= 512) return launch_topk_n<8>(T, E, k, routing, splits, partials, bias, te, tw, s);
+    return launch_topk_n<16>(T, E, k, routing, splits, partials, bias, te, tw, s);
 }
 
 }  // namespace moe

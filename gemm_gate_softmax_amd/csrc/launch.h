@@ -14,10 +14,10 @@ namespace moe {
 int gate_splits(int dt, int T, int H, int E);
 hipError_t launch_gate_logits(int dt, int T, int H, int E, const void* x, const void* wg,
                               float* partials, hipStream_t s);
-// Top-k selection and renormalised weights from logits = (sum of the partials in split
-// order) + bias.
-hipError_t launch_topk(int T, int E, int k, int splits, const float* partials, const float* bias,
-                       int32_t* top_experts, float* top_weights, hipStream_t s);
+// Top-k selection and renormalised weights (routing 0 softmax, 1 sigmoid) from logits =
+// (sum of the partials in split order) + bias.
+hipError_t launch_topk(int T, int E, int k, int routing, int splits, const float* partials,
+                       const float* bias, int32_t* top_experts, float* top_weights, hipStream_t s);
 
 size_t pft_ws_bytes(long long N, int E);
 hipError_t launch_pft(int T, int k, int E, const int32_t* top_experts, int32_t* counts,

@@ -22,6 +22,7 @@ MOE_WS_GATE, MOE_WS_PFT, MOE_WS_GEMM, MOE_WS_LAYER = 0, 1, 2, 3
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_VALUE", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_MISALIGNED", 4: "MOE_ERR_WORKSPACE_TOO_SMALL", 5: "MOE_ERR_LAUNCH"}
 
+ROUTING = {"softmax": 0, "sigmoid": 1}   # moe_routing_t
 EXPORTS = ("moe_workspace_bytes", "moe_status_string", "moe_gate_topk", "moe_pft_build",
            "moe_dispatch", "moe_grouped_gemm_swiglu", "moe_combine", "moe_layer_forward")
 
@@ -55,12 +56,12 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.restype = sz
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
-        L.moe_gate_topk.argtypes = [i32] * 5 + [vp] * 6 + [sz, vp]
+        L.moe_gate_topk.argtypes = [i32] * 6 + [vp] * 6 + [sz, vp]
         L.moe_pft_build.argtypes = [i32] * 3 + [vp] * 7 + [sz, vp]
         L.moe_dispatch.argtypes = [i32] * 4 + [vp] * 4
         L.moe_grouped_gemm_swiglu.argtypes = [i32] * 5 + [vp] * 8 + [sz, vp]
         L.moe_combine.argtypes = [i32] * 4 + [vp] * 5
-        L.moe_layer_forward.argtypes = ([i32] * 6 + [vp] * 7 + [ctypes.POINTER(LayerBufs), vp, sz, vp])
+        L.moe_layer_forward.argtypes = ([i32] * 7 + [vp] * 7 + [ctypes.POINTER(LayerBufs), vp, sz, vp])
         for f in EXPORTS[2:]:
             getattr(L, f).restype = i32
         _lib = L
@@ -122,8 +123,10 @@ def workspace(kind: int, T, H, E, F, k, dt: int, device) -> torch.Tensor:
 
 # -------------------------------------------------------------------------- entries
 
-def moe_gate_topk(x, wg, bias, k, top_experts=None, top_weights=None, ws=None, stream=None):
-    """Top-k softmax gate.  Returns (top_experts [T,k] int32, top_weights [T,k] fp32)."""
+def moe_gate_topk(x, wg, bias, k, top_experts=None, top_weights=None, ws=None, stream=None,
+                  routing="softmax"):
+    """Top-k gate (routing "softmax" or "sigmoid").  Returns (top_experts [T,k] int32,
+    top_weights [T,k] fp32)."""
     dt = dtype_code(x.dtype)
     T, H = x.shape
     E = wg.shape[0]
@@ -136,7 +139,8 @@ def moe_gate_topk(x, wg, bias, k, top_experts=None, top_weights=None, ws=None, s
     _need(top_experts, "top_experts", torch.int32, (T, k))
     _need(top_weights, "top_weights", torch.float32, (T, k))
     ws = workspace(MOE_WS_GATE, T, H, E, 64, k, dt, dev) if ws is None else ws
-    _check("moe_gate_topk", lib().moe_gate_topk(dt, T, H, E, k, _ptr(x), _ptr(wg), _ptr(bias),
+    _check("moe_gate_topk", lib().moe_gate_topk(dt, T, H, E, k, ROUTING[routing], _ptr(x),
+                                                _ptr(wg), _ptr(bias),
                                                 _ptr(top_experts), _ptr(top_weights), _ptr(ws),
                                                 ws.numel() * ws.element_size(), _stream(stream)))
     return top_experts, top_weights
@@ -237,7 +241,7 @@ def alloc_layer_bufs(T, H, E, F, k, dtype, device, fuse_dispatch=False) -> dict:
 
 
 def moe_layer_forward(x, wg, bias, w1, w3, w2, k, out=None, bufs=None, ws=None, stream=None,
-                      fuse_dispatch=False):
+                      fuse_dispatch=False, routing="softmax"):
     """Whole layer.  Returns (out [T,H], bufs dict of intermediates, ws).  With
     fuse_dispatch (or bufs["xd"] None) the dispatch is fused into the expert product."""
     dt = dtype_code(x.dtype)
@@ -255,6 +259,7 @@ def moe_layer_forward(x, wg, bias, w1, w3, w2, k, out=None, bufs=None, ws=None, 
     ws = workspace(MOE_WS_LAYER, T, H, E, F, k, dt, x.device) if ws is None else ws
     cb = LayerBufs(*[_ptr(bufs[n]) for n, _ in LayerBufs._fields_])
     _check("moe_layer_forward", lib().moe_layer_forward(
-        dt, T, H, E, F, k, _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out),
+        dt, T, H, E, F, k, ROUTING[routing], _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3),
+        _ptr(w2), _ptr(out),
         ctypes.byref(cb), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out, bufs, ws

@@ -58,6 +58,11 @@ CONFIGS = {
                                dtype="bf16"),
     "xmoe_large": LayerConfig("xmoe_large", T=4096, H=7168, E=256, F=2048, k=8, dtype="bf16",
                               bias=("zipf", 1.2)),
+    # X-MoE review, 模型配置 table, "Super" row (seq 4096, H 7168, FFN 2560, 256 experts,
+    # top-8); no routing skew is given for it, so the Large row's Zipf(1.2) gate bias is
+    # reused.  Not one of the benchmark configurations: a parity case at a wider F.
+    "xmoe_super": LayerConfig("xmoe_super", T=4096, H=7168, E=256, F=2560, k=8, dtype="bf16",
+                              bias=("zipf", 1.2)),
 }
 
 

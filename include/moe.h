@@ -53,6 +53,16 @@ typedef enum {
     MOE_ERR_LAUNCH = 5               /* the HIP runtime refused a launch */
 } moe_status_t;
 
+/*
+ * Routing function of the gate (FSMoE report, 第六部分: the routing functions a layer may
+ * use include softmax and sigmoid).  Both select the k experts with the largest logits;
+ * they differ in the weights (see moe_gate_topk).
+ */
+typedef enum {
+    MOE_ROUTE_SOFTMAX = 0,
+    MOE_ROUTE_SIGMOID = 1
+} moe_routing_t;
+
 /* Which call a workspace is for (argument of moe_workspace_bytes). */
 typedef enum {
     MOE_WS_GATE = 0,
@@ -74,16 +84,20 @@ const char *moe_status_string(moe_status_t status);
  * form, no dense dispatch mask; FSMoE report, 第三部分 item 1, Gating Function module).
  *   logit[t][e]        = sum_h x[t][h] * wg[e][h] + bias[e]          (fp32 accumulate)
  *   top_experts[t][j]  = the j-th expert in the order (logit desc, expert id asc), j < k
- *   top_weights[t][j]  = softmax(logit[t])[pick j] renormalised over the k picks
- *                      = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)
+ *   top_weights[t][j]  = MOE_ROUTE_SOFTMAX: softmax(logit[t])[pick j] renormalised over
+ *                        the k picks = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)
+ *                      = MOE_ROUTE_SIGMOID: s_j / sum_{i<k} s_i,  s = 1 / (1 + exp(-l))
+ *                        (the pages name sigmoid routing without a formula: this is the
+ *                        plainest reading, renormalised like the softmax route)
  * bias may be NULL (no bias).  Outputs: top_experts [T][k] int32, top_weights [T][k] fp32.
  * ws: moe_workspace_bytes(MOE_WS_GATE, ...) bytes (depends on T, H, E and dt: it holds
  * fp32 partial logits over up to 8 splits of the hidden dimension, which the top-k step
  * adds in split order before the bias).
  */
-moe_status_t moe_gate_topk(moe_dtype_t dt, int T, int H, int E, int k, const void *x,
-                           const void *wg, const float *bias, int32_t *top_experts,
-                           float *top_weights, void *ws, size_t ws_bytes, void *stream);
+moe_status_t moe_gate_topk(moe_dtype_t dt, int T, int H, int E, int k, moe_routing_t routing,
+                           const void *x, const void *wg, const float *bias,
+                           int32_t *top_experts, float *top_weights, void *ws, size_t ws_bytes,
+                           void *stream);
 
 /*
  * Padding-free token buffers (X-MoE review, 训练流程 step 1: flatten top_experts and sort
@@ -166,8 +180,9 @@ typedef struct moe_layer_bufs {
  * is the error word of moe_pft_build.
  */
 moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k,
-                               const void *x, const void *wg, const float *bias,
-                               const void *w1, const void *w3, const void *w2, void *out,
+                               moe_routing_t routing, const void *x, const void *wg,
+                               const float *bias, const void *w1, const void *w3,
+                               const void *w2, void *out,
                                const moe_layer_bufs *bufs, void *ws, size_t ws_bytes,
                                void *stream);
 

@@ -45,12 +45,12 @@ def lib() -> ctypes.CDLL:
             build()
         L = ctypes.CDLL(_LIB)
         vp, i32, lng = ctypes.c_void_p, ctypes.c_int, ctypes.c_long
-        L.oracle_gate_topk.argtypes = [i32] * 5 + [vp] * 7
+        L.oracle_gate_topk.argtypes = [i32] * 6 + [vp] * 7
         L.oracle_pft_build.argtypes = [i32] * 3 + [vp] * 6
         L.oracle_dispatch.argtypes = [i32] * 4 + [vp] * 3
         L.oracle_grouped_gemm_swiglu.argtypes = [i32] * 5 + [vp] * 7
         L.oracle_combine.argtypes = [i32] * 4 + [vp] * 4
-        L.oracle_layer_forward.argtypes = [i32] * 6 + [vp] * 8
+        L.oracle_layer_forward.argtypes = [i32] * 7 + [vp] * 8
         L.oracle_round_bf16.argtypes = [vp, vp, lng]
         L.oracle_num_threads.argtypes = []
         for f in ("oracle_gate_topk", "oracle_pft_build", "oracle_dispatch",
@@ -90,7 +90,10 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
     return out
 
 
-def gate_topk(dt, x, wg, bias, k, want_logits=False):
+ROUTING = {"softmax": 0, "sigmoid": 1}
+
+
+def gate_topk(dt, x, wg, bias, k, want_logits=False, routing="softmax"):
     """Returns (top_experts [T,k] i32, top_weights [T,k] f32[, logits f32, logits f64])."""
     st = _storage(dt)
     x, wg = _c(x, st), _c(wg, st)
@@ -101,8 +104,8 @@ def gate_topk(dt, x, wg, bias, k, want_logits=False):
     tw = np.empty((T, k), np.float32)
     l32 = np.empty((T, E), np.float32) if want_logits else None
     l64 = np.empty((T, E), np.float64) if want_logits else None
-    _check(lib().oracle_gate_topk(_DT[dt], T, H, E, k, _p(x), _p(wg), _p(b), _p(te), _p(tw),
-                                  _p(l32), _p(l64)), "gate_topk")
+    _check(lib().oracle_gate_topk(_DT[dt], T, H, E, k, ROUTING[routing], _p(x), _p(wg), _p(b),
+                                  _p(te), _p(tw), _p(l32), _p(l64)), "gate_topk")
     return (te, tw, l32, l64) if want_logits else (te, tw)
 
 
@@ -158,7 +161,7 @@ def combine(dt, y, dest_pos, top_weights):
     return out
 
 
-def layer_forward(dt, x, wg, bias, w1, w3, w2, k, stage_seconds=False):
+def layer_forward(dt, x, wg, bias, w1, w3, w2, k, stage_seconds=False, routing="softmax"):
     st = _storage(dt)
     x, wg = _c(x, st), _c(wg, st)
     w1, w3, w2 = _c(w1, st), _c(w3, st), _c(w2, st)
@@ -167,6 +170,7 @@ def layer_forward(dt, x, wg, bias, w1, w3, w2, k, stage_seconds=False):
     E, F = w1.shape[0], w1.shape[1]
     out = np.empty((T, H), st)
     secs = np.zeros(5, np.float64)
-    _check(lib().oracle_layer_forward(_DT[dt], T, H, E, F, k, _p(x), _p(wg), _p(b), _p(w1),
-                                      _p(w3), _p(w2), _p(out), _p(secs)), "layer_forward")
+    _check(lib().oracle_layer_forward(_DT[dt], T, H, E, F, k, ROUTING[routing], _p(x), _p(wg),
+                                      _p(b), _p(w1), _p(w3), _p(w2), _p(out), _p(secs)),
+           "layer_forward")
     return (out, secs) if stage_seconds else out

@@ -111,14 +111,20 @@ void oracle_round_bf16(const double *in, uint16_t *out, long n) {
  * Gating Function module; [FDMOE] 1.1, each token picks a few experts).
  *   logit[t][e] = fp32( sum_h x[t][h] * Wg[e][h] + bias[e] )       (double sum)
  *   picks       = the k experts first in the order (logit desc, expert id asc)
- *   weight[t][j]= p(pick j) / sum_{i<k} p(pick i),  p = softmax over all E logits
+ *   routing 0 (softmax top-k, [FSMOE] 第六部分 routing functions, the X-MoE configs):
+ *     weight[t][j] = p(pick j) / sum_{i<k} p(pick i),  p = softmax over all E logits
+ *   routing 1 (sigmoid top-k, [FSMOE] 第六部分 lists Sigmoid routing; the pages give no
+ *   formula, read here as the plainest form): each expert scores sigmoid(logit), the
+ *   picks are the same (sigmoid is increasing), and their scores are renormalised:
+ *     weight[t][j] = s(pick j) / sum_{i<k} s(pick i),  s = 1 / (1 + exp(-logit))
  * Outputs top_experts[T][k] (int32), top_weights[T][k] (fp32); optionally the fp32
  * logits [T][E] and the unrounded double logits [T][E].
  */
-int oracle_gate_topk(int dt, int T, int H, int E, int k, const void *x, const void *wg,
+int oracle_gate_topk(int dt, int T, int H, int E, int k, int routing, const void *x, const void *wg,
                      const float *bias, int32_t *top_experts, float *top_weights,
                      float *logits_out, double *logits64_out) {
     if (!valid_dtype(dt) || T < 0 || H <= 0 || E <= 0 || k < 1 || k > E) return OR_EINVAL;
+    if (routing != 0 && routing != 1) return OR_EINVAL;
     int err = OR_OK;
 #pragma omp parallel for schedule(dynamic, 4)
     for (int t = 0; t < T; ++t) {
@@ -148,10 +154,16 @@ int oracle_gate_topk(int dt, int T, int H, int E, int k, const void *x, const vo
             }
             order[j] = e;
         }
-        /* Softmax over all E, then renormalise over the k picks. */
-        double m = (double)l[order[0]], z = 0.0, zsel = 0.0;
-        for (int e = 0; e < E; ++e) z += exp((double)l[e] - m);
-        for (int e = 0; e < E; ++e) p[e] = exp((double)l[e] - m) / z;
+        if (routing == 0) {
+            /* Softmax over all E, then renormalise over the k picks. */
+            double m = (double)l[order[0]], z = 0.0;
+            for (int e = 0; e < E; ++e) z += exp((double)l[e] - m);
+            for (int e = 0; e < E; ++e) p[e] = exp((double)l[e] - m) / z;
+        } else {
+            /* Sigmoid score of every expert. */
+            for (int e = 0; e < E; ++e) p[e] = 1.0 / (1.0 + exp(-(double)l[e]));
+        }
+        double zsel = 0.0;
         for (int j = 0; j < k; ++j) zsel += p[order[j]];
         for (int j = 0; j < k; ++j) {
             top_experts[(size_t)t * k + j] = order[j];
@@ -315,11 +327,12 @@ static double wall_seconds(void) {
     return (double)ts.tv_sec + 1e-9 * (double)ts.tv_nsec;
 }
 
-int oracle_layer_forward(int dt, int T, int H, int E, int F, int k, const void *x,
+int oracle_layer_forward(int dt, int T, int H, int E, int F, int k, int routing, const void *x,
                          const void *wg, const float *bias, const void *w1, const void *w3,
                          const void *w2, void *out, double *stage_seconds) {
     if (!valid_dtype(dt) || T < 0 || H <= 0 || E < 1 || F <= 0 || k < 1 || k > E)
         return OR_EINVAL;
+    if (routing != 0 && routing != 1) return OR_EINVAL;
     long N = (long)T * k;
     size_t es = elem_size(dt);
     int32_t *te = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N ? N : 1));
@@ -337,7 +350,7 @@ int oracle_layer_forward(int dt, int T, int H, int E, int F, int k, const void *
 #define STAGE_BEGIN() do { t0 = wall_seconds(); } while (0)
 #define STAGE_END(i) do { t1 = wall_seconds(); if (stage_seconds) stage_seconds[i] = t1 - t0; } while (0)
     STAGE_BEGIN();
-    rc = oracle_gate_topk(dt, T, H, E, k, x, wg, bias, te, tw, NULL, NULL);
+    rc = oracle_gate_topk(dt, T, H, E, k, routing, x, wg, bias, te, tw, NULL, NULL);
     STAGE_END(0);
     if (rc) goto done;
     STAGE_BEGIN();

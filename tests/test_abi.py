@@ -71,17 +71,18 @@ MIS = P(0x10004)
 
 def test_gate_rejects(L):
     g = L.moe_gate_topk
-    assert g(1, 8, 64, 4, 5, A, A, None, A, A, A, 1 << 20, None) == UNSUPPORTED      # k > E
-    assert g(1, 8, 64, 4, 0, A, A, None, A, A, A, 1 << 20, None) == INVALID          # k < 1
-    assert g(1, 8, 96, 4, 2, A, A, None, A, A, A, 1 << 20, None) == UNSUPPORTED      # H % 64
-    assert g(1, 8, 64, 2048, 2, A, A, None, A, A, A, 1 << 30, None) == UNSUPPORTED   # E > max
-    assert g(3, 8, 64, 4, 2, A, A, None, A, A, A, 1 << 20, None) == INVALID          # dtype
-    assert g(1, 8, 64, 4, 2, None, A, None, A, A, A, 1 << 20, None) == INVALID       # NULL x
-    assert g(1, 8, 64, 4, 2, MIS, A, None, A, A, A, 1 << 20, None) == MISALIGNED
-    assert g(1, 8, 64, 4, 2, A, A, MIS, A, A, A, 1 << 20, None) == MISALIGNED        # bias
-    assert g(1, 8, 64, 4, 2, A, A, None, A, A, A, 16, None) == WS_SMALL
-    assert g(1, 0, 64, 4, 2, None, None, None, None, None, None, 0, None) == OK      # T == 0
-    assert g(1, -1, 64, 4, 2, A, A, None, A, A, A, 1 << 20, None) == INVALID
+    assert g(1, 8, 64, 4, 5, 0, A, A, None, A, A, A, 1 << 20, None) == UNSUPPORTED      # k > E
+    assert g(1, 8, 64, 4, 0, 0, A, A, None, A, A, A, 1 << 20, None) == INVALID          # k < 1
+    assert g(1, 8, 96, 4, 2, 0, A, A, None, A, A, A, 1 << 20, None) == UNSUPPORTED      # H % 64
+    assert g(1, 8, 64, 2048, 2, 0, A, A, None, A, A, A, 1 << 30, None) == UNSUPPORTED   # E > max
+    assert g(3, 8, 64, 4, 2, 0, A, A, None, A, A, A, 1 << 20, None) == INVALID          # dtype
+    assert g(1, 8, 64, 4, 2, 0, None, A, None, A, A, A, 1 << 20, None) == INVALID       # NULL x
+    assert g(1, 8, 64, 4, 2, 0, MIS, A, None, A, A, A, 1 << 20, None) == MISALIGNED
+    assert g(1, 8, 64, 4, 2, 0, A, A, MIS, A, A, A, 1 << 20, None) == MISALIGNED        # bias
+    assert g(1, 8, 64, 4, 2, 0, A, A, None, A, A, A, 16, None) == WS_SMALL
+    assert g(1, 0, 64, 4, 2, 0, None, None, None, None, None, None, 0, None) == OK      # T == 0
+    assert g(1, -1, 64, 4, 2, 0, A, A, None, A, A, A, 1 << 20, None) == INVALID
+    assert g(1, 8, 64, 4, 2, 2, A, A, None, A, A, A, 1 << 20, None) == INVALID       # routing
 
 
 def test_pft_rejects(L):
@@ -121,9 +122,11 @@ def test_gemm_and_layer_reject(L):
     lf = L.moe_layer_forward
     bufs = ops.LayerBufs(*([A] * 10))
     args = lambda **kw: [kw.get("dt", 1), kw.get("T", 8), kw.get("H", 64), kw.get("E", 4),
-                         kw.get("F", 64), kw.get("k", 2), A, A, None, A, A, A, A,
+                         kw.get("F", 64), kw.get("k", 2), kw.get("routing", 0), A, A, None, A,
+                         A, A, A,
                          ctypes.byref(kw.get("bufs", bufs)), A, kw.get("ws", 1 << 30), None]
     assert lf(*args(k=5)) == UNSUPPORTED
+    assert lf(*args(routing=7)) == INVALID
     assert lf(*args(F=32)) == UNSUPPORTED
     assert lf(*args(ws=100)) == WS_SMALL
     nb = ops.LayerBufs(*([A] * 9 + [None]))

@@ -229,6 +229,43 @@ def test_layer_parity_small(orc, cfg):
     assert int(host(ws[:4].view(torch.int32))[0]) == 0
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,H,E,k", [(200, 256, 8, 2), (333, 512, 64, 6), (256, 1024, 256, 8)])
+def test_gate_sigmoid_parity(orc, dt, T, H, E, k):
+    cfg = W.LayerConfig("g", T=T, H=H, E=E, F=64, k=k, dtype=dt, bias=("zipf", 1.0))
+    g = W.make_gate_inputs(cfg, seed=T + E + 1)
+    te_ref, tw_ref, _, l64 = orc.gate_topk(dt, g["x"], g["wg"], g["bias"], k, want_logits=True,
+                                           routing="sigmoid")
+    te, tw = ops.moe_gate_topk(dev(g["x"], dt), dev(g["wg"], dt), dev(g["bias"]), k,
+                               routing="sigmoid")
+    te, tw = host(te), host(tw)
+    r = compare_routing(te, te_ref, l64, k)
+    _log(f"gate sigmoid {dt} T={T} H={H} E={E} k={k}: mismatches {len(r['mismatch'])} "
+         f"(near-tie {len(r['tie_exact'])}, accumulation band {len(r['tie_acc'])})")
+    assert len(r["bad"]) == 0
+    ok = np.setdiff1d(np.arange(T), r["mismatch"])
+    assert np.max(np.abs(tw[ok] - tw_ref[ok])) <= WEIGHT_ATOL
+
+
+@pytest.mark.parametrize("cfg", SMALL_LAYERS[1:], ids=lambda c: c.name)
+def test_layer_sigmoid_routing_small(orc, cfg):
+    d = W.make_host(cfg, seed=3)
+    dt = cfg.dtype
+    ref = orc.layer_forward(dt, d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k,
+                            routing="sigmoid")
+    te_ref, _, _, l64 = orc.gate_topk(dt, d["x"], d["wg"], d["bias"], cfg.k, want_logits=True,
+                                      routing="sigmoid")
+    out, bufs, _ = ops.moe_layer_forward(dev(d["x"], dt), dev(d["wg"], dt), dev(d["bias"]),
+                                         dev(d["w1"], dt), dev(d["w3"], dt), dev(d["w2"], dt),
+                                         cfg.k, routing="sigmoid", fuse_dispatch=True)
+    r = compare_routing(host(bufs["top_experts"]), te_ref, l64, cfg.k)
+    assert len(r["bad"]) == 0
+    ok = np.setdiff1d(np.arange(cfg.T), r["mismatch"])
+    err = max_abs_rel(host(out, dt)[ok], ref[ok], dt)
+    _log(f"layer sigmoid {cfg.name}: out err {err:.2e}")
+    assert err <= TOL[dt]
+
+
 def test_layer_deterministic():
     cfg = SMALL_LAYERS[1]
     d = W.make_device(cfg, seed=1, device=DEV)
@@ -278,7 +315,7 @@ def test_rejects_bad_arguments_on_device():
 
 # --------------------------------------------------------- full sizes, sampled outputs
 
-FULL = ["top2_f32", "xmoe_small", "xmoe_medium", "xmoe_large"]
+FULL = ["top2_f32", "xmoe_small", "xmoe_medium", "xmoe_large", "xmoe_super"]
 
 
 def _expert_host(d, e, dt):

@@ -145,6 +145,45 @@ def test_gate_weights_closed_form(orc, k):
         assert np.allclose(tw[t], ref, rtol=2 ** -23, atol=0)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_sigmoid_routing_selects_like_softmax(orc, dt):
+    # both scores increase with the logit, so the picks (and their order) are the same
+    rng = np.random.default_rng(23)
+    T, H, E, k = 300, 64, 48, 5
+    x = W._store(rng.standard_normal((T, H)), dt)
+    wg = W._store(rng.standard_normal((E, H)) / 8, dt)
+    bias = rng.standard_normal(E).astype(np.float32)
+    te_soft, tw_soft = orc.gate_topk(dt, x, wg, bias, k)
+    te_sig, tw_sig = orc.gate_topk(dt, x, wg, bias, k, routing="sigmoid")
+    assert np.array_equal(te_soft, te_sig)
+    assert np.all(np.abs(tw_sig.astype(np.float64).sum(1) - 1.0) <= k * 2.0 ** -24)
+    assert np.all(np.diff(tw_sig, axis=1) <= 0)
+    assert not np.allclose(tw_soft, tw_sig)          # a different routing function
+
+
+def test_sigmoid_routing_closed_forms(orc):
+    # Wg = 0 makes the logits equal the bias exactly; sigmoid(ln 3) = 3/4, sigmoid(0) = 1/2,
+    # sigmoid(-ln 3) = 1/4, so the renormalised picks are plain fractions.
+    ln3 = math.log(3.0)
+    x = np.ones((1, 64), np.float32)
+    wg = np.zeros((4, 64), np.float32)
+    bias = np.array([0.0, -ln3, ln3, -5.0], np.float32)
+    cases = {1: [2], 2: [2, 0], 3: [2, 0, 1]}
+    want = {1: [1.0], 2: [0.6, 0.4], 3: [0.5, 1 / 3, 1 / 6]}
+    for k, picks in cases.items():
+        te, tw = orc.gate_topk("f32", x, wg, bias, k, routing="sigmoid")
+        assert te[0].tolist() == picks
+        assert np.allclose(tw[0], want[k], rtol=0, atol=1e-6)
+    # a symmetric pair keeps the raw sigmoid values (they already sum to 1); softmax routing
+    # of the same logits gives 9/10 and 1/10 instead
+    te, tw = orc.gate_topk("f32", x[:, :64], np.zeros((2, 64), np.float32),
+                           np.array([ln3, -ln3], np.float32), 2, routing="sigmoid")
+    assert np.allclose(tw[0], [0.75, 0.25], rtol=0, atol=1e-6)
+    te, tw = orc.gate_topk("f32", x[:, :64], np.zeros((2, 64), np.float32),
+                           np.array([ln3, -ln3], np.float32), 2)
+    assert np.allclose(tw[0], [0.9, 0.1], rtol=0, atol=1e-6)
+
+
 # ------------------------------------------------------------------ padding-free buffers
 
 def test_pft_hand_example(orc):
@@ -340,6 +379,10 @@ def test_layer_matches_dense_capacity_formulation(orc, dt):
 
 def test_oracle_rejects_bad_arguments(orc):
     x = np.zeros((4, 8), np.float32)
+    with pytest.raises(KeyError):
+        orc.gate_topk("f32", x, np.zeros((3, 8), np.float32), None, 2, routing="relu")
+    # an unknown routing id is rejected before any pointer is touched
+    assert orc.lib().oracle_gate_topk(0, 4, 8, 3, 2, 5, *([None] * 7)) != 0
     with pytest.raises(RuntimeError):
         orc.gate_topk("f32", x, np.zeros((3, 8), np.float32), None, 4)     # k > E
     with pytest.raises(RuntimeError):
