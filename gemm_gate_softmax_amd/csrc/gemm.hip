@@ -11,10 +11,14 @@
 // K (activations [rows][K], weights [features][K]).  NB = 2 fuses the SwiGLU gate and up
 // products so the epilogue forms silu(a) * g in registers.
 //
-// Every tile is 128 tokens x (128 x NB or 256) features, its operands staged through an
-// LDS ring by direct-to-LDS transfers and consumed by 4 waves in a 2 x 2 layout.  An
-// expert with a handful of rows still gets a whole tile: its time goes to streaming the
-// expert's weights, which measured no slower through this path than through registers.
+// Every tile is 128 tokens x (128 x NB or 256) features.  A workgroup is 4 loader waves,
+// which stage the operands through an LDS ring with direct-to-LDS transfers, and 4
+// compute waves in a 2 x 2 layout, which read the ring and issue the MFMAs.  An expert
+// with a handful of rows still gets a whole tile (its MFMAs and activation transfers for
+// empty token columns are skipped): its time goes to streaming the expert's weights, which
+// measured no slower through this path than through registers.  The up product can
+// gather its activation rows from the token rows through token_ids, which fuses the
+// dispatch into it.
 #include "device.h"
 #include "launch.h"
 
@@ -27,8 +31,8 @@ enum Epilogue { kEpiLogits = 0, kEpiSwiGLU = 1, kEpiStore = 2 };
 
 // Tile shapes.  Expert products: 128 tokens; up product 128 features x 2 operands, down
 // product 256 features; a 3-slot ring of 48 KiB k-slices (64 k per row, whole 128-byte
-// lines).  The gate logits use small 64 x 64 tiles so a few thousand tokens still fill
-// the chip.
+// lines).  The gate logits use small 64 x 64 tiles over K splits so a few thousand tokens
+// still fill the chip.  The macros exist to build variants for measurement.
 #ifndef MOE_EXPERT_BTOK
 #define MOE_EXPERT_BTOK 128
 #define MOE_EXPERT_UP_BF 128
@@ -42,7 +46,7 @@ constexpr int kExpertUpBF = MOE_EXPERT_UP_BF;
 constexpr int kExpertDownBF = MOE_EXPERT_DOWN_BF;
 constexpr int kExpertStages = MOE_EXPERT_STAGES;
 constexpr int kExpertRowBytes = MOE_EXPERT_RB;
-constexpr int kGroupTok = MOE_GROUP_TOK;      // token tiles per L2-sharing block (see expert_tile_of)
+constexpr int kGroupTok = MOE_GROUP_TOK;   // token tiles per L2-sharing block (expert_gemm_kernel)
 
 template <typename T, int NB>
 struct GemmParams {
@@ -55,15 +59,16 @@ struct GemmParams {
     long long w_stride;     // elements per expert
     int n_feat;             // output features (weight rows per expert)
     int feat_tiles;         // compute tiles per token tile: ceil(n_feat / BF)
-    const int4* table;      // compute token tiles: (expert, first tile of expert, row0, rows)
+    const int4* table;      // token tiles: (expert, first entry of the expert, row0, rows)
     const int* table_count; // entries in table
     int dense_rows;         // rows of the single expert of a dense product (gate)
-    void* out;              // [rows][n_feat]: fp32 logits or storage type
-    int k_slices;           // dense product: k-slices per K split (0: the whole K)
+    void* out;              // [rows][n_feat]: fp32 partial logits or storage type
+    int k_slices;           // dense product: k-slices per K split
 };
 
-// Writes 4 consecutive features of one token: fp32 logits (+ bias, per-element bounds),
-// or the storage type (n_feat is a multiple of 64, so a run never straddles the end).
+// Writes 4 consecutive features of one token: fp32 partial logits (per-element bounds; the
+// top-k step adds the bias), or the storage type (n_feat is a multiple of 64 there, so a
+// run never straddles the end).
 template <typename T, int NB, int EPI>
 __device__ __forceinline__ void store_run(const GemmParams<T, NB>& p, int tok, int feat,
                                           const float (&r)[4]) {
