@@ -27,7 +27,6 @@ summary and is reported only while the kernel sources still hash to what was pro
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -41,7 +40,6 @@ METRIC = "MoE layer fwd tokens/s + grouped-GEMM % MFMA peak, X-MoE Large, 1 GPU"
 HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, published
 UP_KERNEL = "expert_gemm_kernel<moe::bf16_t, 2, 1"   # name prefix in profiler output
-KERNEL_SOURCES = ("gemm_gate_softmax_amd/csrc/gemm.hip", "gemm_gate_softmax_amd/csrc/device.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "xmoe_large_expert_up_traffic.md")
 COPY_BYTES = 1 << 30
 
@@ -69,12 +67,9 @@ def parse():
 
 
 def kernel_digest():
-    """sha256 over the expert kernel's sources: counter readings are tied to it."""
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    """sha256 over the expert kernel's code: counter readings are tied to it."""
+    from gemm_gate_softmax_amd.profile_summary import kernel_digest as digest
+    return digest()
 
 
 def recorded_traffic(workload):

@@ -22,6 +22,7 @@ import argparse
 import csv
 import hashlib
 import os
+import re
 import statistics
 import sys
 
@@ -42,11 +43,21 @@ def _short(name, width=96):
     return name if len(name) <= width else name[:width - 3] + "..."
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace runs collapsed (string literals
+    in these files hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_digest():
+    """sha256 over the expert kernel's code (comments and layout ignored): the traffic
+    counters recorded in profiles/ are tied to it."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
