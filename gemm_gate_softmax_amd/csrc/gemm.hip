@@ -11,12 +11,13 @@
 // K (activations [rows][K], weights [features][K]).  NB = 2 fuses the SwiGLU gate and up
 // products so the epilogue forms silu(a) * g in registers.
 //
-// Every tile is 128 tokens x (128 x NB or 256) features.  A workgroup is 4 loader waves,
-// which stage the operands through an LDS ring with direct-to-LDS transfers, and 4
-// compute waves in a 2 x 2 layout, which read the ring and issue the MFMAs.  An expert
-// with a handful of rows still gets a whole tile (its MFMAs and activation transfers for
-// empty token columns are skipped): its time goes to streaming the expert's weights, which
-// measured no slower through this path than through registers.  The up product can
+// An expert tile is 128 tokens x (128 x NB or 256) features, or 64 tokens for an expert
+// with at most 64 rows.  A workgroup is 4 loader waves, which stage the operands through
+// an LDS ring with direct-to-LDS transfers, and 4 compute waves in a 2 x 2 layout, which
+// read the ring and issue the MFMAs.  An expert with a handful of rows still gets a whole
+// tile (its MFMAs and activation transfers for empty token columns are skipped): its time
+// goes to streaming the expert's weights, which measured no slower through this path than
+// through registers.  The up product can
 // gather its activation rows from the token rows through token_ids, which fuses the
 // dispatch into it.
 #include "device.h"
@@ -33,6 +34,10 @@ enum Epilogue { kEpiLogits = 0, kEpiSwiGLU = 1, kEpiStore = 2 };
 // product 256 features; a 3-slot ring of 48 KiB k-slices (64 k per row, whole 128-byte
 // lines).  The gate logits use small 64 x 64 tiles over K splits so a few thousand tokens
 // still fill the chip.  The macros exist to build variants for measurement.
+#ifndef MOE_SMALL_BTOK
+#define MOE_SMALL_BTOK 64      // 0: no small tiles
+#define MOE_SMALL_STAGES 3
+#endif
 #ifndef MOE_EXPERT_BTOK
 #define MOE_EXPERT_BTOK 128
 #define MOE_EXPERT_UP_BF 128
@@ -47,6 +52,17 @@ constexpr int kExpertDownBF = MOE_EXPERT_DOWN_BF;
 constexpr int kExpertStages = MOE_EXPERT_STAGES;
 constexpr int kExpertRowBytes = MOE_EXPERT_RB;
 constexpr int kGroupTok = MOE_GROUP_TOK;   // token tiles per L2-sharing block (expert_gemm_kernel)
+// Experts with at most kSmallBTok rows get one small tile: kSmallBTok tokens, the same
+// features, a kSmallStages-slot ring.  Such a tile is mostly a weight stream; in its own
+// list it can be spread evenly among the MFMA-heavy tiles of the large experts, and its
+// MFMAs are shared by all four compute waves (a 128-token tile leaves two of them idle).
+// Its weights, which no other tile reads, are loaded non-temporal so they do not displace
+// the large tiles' shared operands from L2.  Measured on the X-MoE Large routing: grouped
+// GEMM 4.58 -> 4.57 ms for the separate list, -> 4.40 ms with the non-temporal weights
+// (same box); a fourth ring slot for the small tile (the LDS it frees allows one) changed
+// nothing.
+constexpr int kSmallBTok = MOE_SMALL_BTOK;
+constexpr int kSmallStages = MOE_SMALL_STAGES;
 
 template <typename T, int NB>
 struct GemmParams {
@@ -60,7 +76,8 @@ struct GemmParams {
     int n_feat;             // output features (weight rows per expert)
     int feat_tiles;         // compute tiles per token tile: ceil(n_feat / BF)
     const int4* table;      // token tiles: (expert, first entry of the expert, row0, rows)
-    const int* table_count; // entries in table
+    const int4* stable;     // small-tile experts: (expert, entry, row0, rows)
+    const int* table_count; // [0] entries in table, [1] entries in stable
     int dense_rows;         // rows of the single expert of a dense product (gate)
     void* out;              // [rows][n_feat]: fp32 partial logits or storage type
     int k_slices;           // dense product: k-slices per K split
@@ -100,6 +117,14 @@ __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a));
 // each LDS read); the ring's waits are explicit (wait_vm_and_barrier).
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_block) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "{m0}"(lds_block)
+                 : "memory");
+}
+
+// The same with the non-temporal hint, for data read exactly once.
+__device__ __forceinline__ void dma16_nt(const void* src, uint32_t lds_block) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                  :
                  : "v"(src), "{m0}"(lds_block)
                  : "memory");
@@ -157,8 +182,9 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
 // compute wave that shares a SIMD with a loader keeps its MFMAs going meanwhile.  One
 // barrier per stage hands the slots over: before barrier kt every loader has seen stage kt
 // land and every compute wave has finished reading stage kt-1, so after it stage kt is
-// read while stage kt+S-1 is loaded into the slot stage kt-1 left.
-template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool FULL>
+// read while stage kt+S-1 is loaded into the slot stage kt-1 left.  WNT marks the weight
+// transfers non-temporal: for a tile that is the only reader of its weights.
+template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool FULL, bool WNT = false>
 __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* lds, int expert,
                                              int row0, int row_end, int f0, int s0, int nk) {
     using Tile = CompTile<BT, BF, NB, S, RB>;
@@ -223,7 +249,8 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
             const uint32_t b_ = __builtin_amdgcn_readfirstlane(wbase + (SLOT) * kStageBytes); \
             const size_t o_ = (size_t)(KT) * kRowBytes;                                      \
             _Pragma("unroll") for (int i_ = 0; i_ < kDma; ++i_)                              \
-                if (i_ >= kActDma || i_ < nact) dma16(src[i_] + o_, b_ + i_ * 4096);          \
+                if (i_ >= kActDma && WNT) dma16_nt(src[i_] + o_, b_ + i_ * 4096);           \
+                else if (i_ >= kActDma || i_ < nact) dma16(src[i_] + o_, b_ + i_ * 4096);     \
         } while (0)
         for (int s = 0; s < S - 1; ++s) MOE_ISSUE(min(s, nk - 1), s);
         // barrier 0: stage 0 landed
@@ -376,67 +403,105 @@ __global__ __launch_bounds__(kThreads, 1) void dense_gemm_kernel(GemmParams<T, N
         compute_tile<T, NB, EPI, BT, BF, S, RB, false>(q, lds, 0, ttile * BT, row_end, ftile * BF, s0, nk);
 }
 
-// Grouped expert product.  XCD x (workgroups x, x + 8, ...) takes a contiguous share of
-// the tiles in dispatch order.  Tiles of one expert go in blocks of kGroupTok token tiles;
-// inside a block the feature tile varies slowest, so the ~32 tiles an XCD runs at once
-// cover about 8 token tiles x 4 feature tiles and share both operands through its L2
-// (measured best among blocks of 2 to 32 on the X-MoE Large routing).
-template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
-__global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, NB> p) {
-    __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, NB, S, RB>::kLdsBytes];
-    const int total = *p.table_count * p.feat_tiles;
-    const int chunk = (total + 7) >> 3;
-    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    if (local >= chunk) return;
-    const int L = xcd * chunk + local;
-    if (L >= total) return;
-    const int4 te = p.table[L / p.feat_tiles];
-    const int expert = te.x, first = te.y, seg0 = te.z, segn = te.w;
-    const int n_e = (segn + BT - 1) / BT;
-    const int q = L - p.feat_tiles * first;
-    const int blk_tiles = kGroupTok * p.feat_tiles;
-    const int blk = min(q / blk_tiles, (n_e - 1) / kGroupTok);
-    const int width = min(kGroupTok, n_e - blk * kGroupTok);
-    const int ql = q - blk * blk_tiles;
-    const int ftile = ql / width;
-    const int ttile = blk * kGroupTok + (ql - ftile * width);
-    const int row0 = seg0 + ttile * BT, row_end = min(seg0 + segn, p.act_rows);
-    const int nk = (int)((size_t)p.K * sizeof(T) / RB);
-    if (row_end - row0 >= BT)
-        compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, expert, row0, row_end, ftile * BF, 0, nk);
-    else
-        compute_tile<T, NB, EPI, BT, BF, S, RB, false>(p, lds, expert, row0, row_end, ftile * BF, 0, nk);
+// Grouped expert product.  Tiles come from two lists: experts with more than kSmallBTok
+// rows (token tiles of BT rows) and experts with at most kSmallBTok rows (one small tile
+// each).  XCD x (workgroups x, x + 8, ...) takes a contiguous share of each list and
+// interleaves the two evenly in dispatch order, so the small tiles' weight streams overlap
+// the large tiles' MFMA work throughout the launch.  Tiles of one large expert go in blocks
+// of kGroupTok token tiles; inside a block the feature tile varies slowest, so the ~32
+// tiles an XCD runs at once cover about 8 token tiles x 4 feature tiles and share both
+// operands through its L2 (measured best among blocks of 2 to 32 on the X-MoE Large
+// routing).
+template <int BT, int BF, int NB, int S, int RB>
+constexpr int expert_lds_bytes() {
+    constexpr int a = CompTile<BT, BF, NB, S, RB>::kLdsBytes;
+    constexpr int b = kSmallBTok > 0 ? CompTile<(kSmallBTok > 0 ? kSmallBTok : 64), BF, NB,
+                                                kSmallStages, RB>::kLdsBytes : 0;
+    return a > b ? a : b;
 }
 
-// Tile table, built on the device from the offsets (no host read of the counts): one
-// entry per BT-row token tile of every expert, (expert, first token tile of that expert,
-// first row, rows); *count = entries.  Segments are clipped to [0, rows) so malformed
-// offsets can never address past the buffers, and no more than cap entries are written.
-// Single workgroup; E <= 1024.
+template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
+__global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, NB> p) {
+    __shared__ __attribute__((aligned(1024))) char lds[expert_lds_bytes<BT, BF, NB, S, RB>()];
+    const int tot_m = p.table_count[0] * p.feat_tiles;
+    const int tot_s = p.table_count[1] * p.feat_tiles;
+    const int chunk_m = (tot_m + 7) >> 3, chunk_s = (tot_s + 7) >> 3;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int m_x = max(0, min(chunk_m, tot_m - xcd * chunk_m));
+    const int s_x = max(0, min(chunk_s, tot_s - xcd * chunk_s));
+    const int n_x = m_x + s_x;
+    if (j >= n_x) return;
+    const int nk = (int)((size_t)p.K * sizeof(T) / RB);
+    // the j-th tile of this XCD is large-list entry a0 when a1 > a0, else small entry j - a0
+    const int a0 = (int)((long long)j * m_x / n_x), a1 = (int)((long long)(j + 1) * m_x / n_x);
+    if (a1 > a0) {
+        const int L = xcd * chunk_m + a0;
+        const int4 te = p.table[L / p.feat_tiles];
+        const int expert = te.x, first = te.y, seg0 = te.z, segn = te.w;
+        const int n_e = (segn + BT - 1) / BT;
+        const int q = L - p.feat_tiles * first;
+        const int blk_tiles = kGroupTok * p.feat_tiles;
+        const int blk = min(q / blk_tiles, (n_e - 1) / kGroupTok);
+        const int width = min(kGroupTok, n_e - blk * kGroupTok);
+        const int ql = q - blk * blk_tiles;
+        const int ftile = ql / width;
+        const int ttile = blk * kGroupTok + (ql - ftile * width);
+        const int row0 = seg0 + ttile * BT, row_end = min(seg0 + segn, p.act_rows);
+        if (row_end - row0 >= BT)
+            compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, expert, row0, row_end, ftile * BF, 0, nk);
+        else
+            compute_tile<T, NB, EPI, BT, BF, S, RB, false>(p, lds, expert, row0, row_end, ftile * BF, 0, nk);
+    } else if constexpr (kSmallBTok > 0) {
+        constexpr int SB = kSmallBTok > 0 ? kSmallBTok : 64;
+        const int Ls = xcd * chunk_s + (j - a0);
+        const int4 te = p.stable[Ls / p.feat_tiles];
+        const int ftile = Ls - (Ls / p.feat_tiles) * p.feat_tiles;
+        const int row0 = te.z, row_end = min(te.z + te.w, p.act_rows);
+        if (row_end - row0 >= SB)
+            compute_tile<T, NB, EPI, SB, BF, kSmallStages, RB, true, true>(p, lds, te.x, row0, row_end, ftile * BF, 0, nk);
+        else
+            compute_tile<T, NB, EPI, SB, BF, kSmallStages, RB, false, true>(p, lds, te.x, row0, row_end, ftile * BF, 0, nk);
+    }
+}
+
+// Tile tables, built on the device from the offsets (no host read of the counts).  An
+// expert with more than `small` rows gets one `table` entry per btok-row token tile,
+// (expert, index of its first entry, first row, rows); an expert with 1..small rows gets
+// one `stable` entry (expert, its index, first row, rows).  count[0], count[1] = entries.
+// Segments are clipped to [0, rows) so malformed offsets can never address past the
+// buffers, and no more than cap (table) or E (stable) entries are written.  Single
+// workgroup; E <= 1024.
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets, int E, int rows,
-                                                          int btok, int cap, int4* table,
-                                                          int* count) {
-    __shared__ int scan[2][1024];
+                                                          int btok, int small, int cap,
+                                                          int4* table, int4* stable, int* count) {
+    __shared__ long long scan[2][1024];
     const int e = threadIdx.x;
-    int beg = 0, cnt = 0, nt = 0;
+    int beg = 0, cnt = 0, nm = 0, ns = 0;
     if (e < E) {
         beg = min(max(offsets[e], 0), rows);
         cnt = max(min(offsets[e + 1], rows) - beg, 0);
-        nt = (cnt + btok - 1) / btok;
+        if (cnt > small) nm = (cnt + btok - 1) / btok;
+        else if (cnt > 0) ns = 1;
     }
-    // inclusive Hillis-Steele scan of the tile counts
+    // inclusive Hillis-Steele scan of (nm, ns) packed in 64 bits
     int cur = 0;
-    scan[0][e] = nt;
+    scan[0][e] = (long long)nm | ((long long)ns << 32);
     __syncthreads();
     for (int d = 1; d < 1024; d <<= 1) {
-        const int v = scan[cur][e] + (e >= d ? scan[cur][e - d] : 0);
+        const long long v = scan[cur][e] + (e >= d ? scan[cur][e - d] : 0);
         scan[cur ^ 1][e] = v;
         cur ^= 1;
         __syncthreads();
     }
-    const int first = scan[cur][e] - nt;
-    for (int j = 0; j < nt && first + j < cap; ++j) table[first + j] = make_int4(e, first, beg, cnt);
-    if (e == 1023) *count = min(scan[cur][e], cap);
+    const long long incl = scan[cur][e];
+    const int first_m = (int)(incl & 0xffffffff) - nm;
+    const int first_s = (int)(incl >> 32) - ns;
+    for (int j = 0; j < nm && first_m + j < cap; ++j) table[first_m + j] = make_int4(e, first_m, beg, cnt);
+    if (ns) stable[first_s] = make_int4(e, first_s, beg, cnt);
+    if (e == 1023) {
+        count[0] = min((int)(incl & 0xffffffff), cap);
+        count[1] = (int)(incl >> 32);
+    }
 }
 
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
@@ -448,8 +513,8 @@ hipError_t launch_dense(const GemmParams<T, NB>& p, int grid, hipStream_t s) {
 }
 
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
-hipError_t launch_expert(const GemmParams<T, NB>& p, int max_tiles, hipStream_t s) {
-    const int grid = (max_tiles + 7) & ~7;
+hipError_t launch_expert(const GemmParams<T, NB>& p, int max_m, int max_s, hipStream_t s) {
+    const int grid = 8 * ((max_m + 7) / 8 + (max_s + 7) / 8);
     if (grid <= 0) return hipSuccess;
     hipLaunchKernelGGL((expert_gemm_kernel<T, NB, EPI, BT, BF, S, RB>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
@@ -492,6 +557,7 @@ hipError_t gate_logits_t(int dt, int T_, int H, int E, const void* x, const void
 struct TableLayout {
     int* count;
     int4* table;
+    int4* stable;
     int cap;
 };
 
@@ -505,6 +571,7 @@ inline TableLayout carve_tables(void* ws, int N, int E) {
     t.count = reinterpret_cast<int*>(w);
     t.cap = (int)tiles_cap(N, E);
     t.table = reinterpret_cast<int4*>(w + 256);
+    t.stable = t.table + t.cap;
     return t;
 }
 
@@ -514,8 +581,9 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
                      const void* w2, void* h, void* y, void* ws, hipStream_t s) {
     constexpr int BT = kExpertBTok;
     const TableLayout tl = carve_tables(ws, N, E);
-    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, N, BT, tl.cap,
-                       tl.table, tl.count);
+    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, N, BT, kSmallBTok,
+                       tl.cap, tl.table, tl.stable, tl.count);
+    const int max_small = kSmallBTok > 0 ? (E < N ? E : N) : 0;
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
@@ -533,10 +601,11 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
     up.n_feat = F;
     up.feat_tiles = (F + UP_BF - 1) / UP_BF;
     up.table = tl.table;
+    up.stable = tl.stable;
     up.table_count = tl.count;
     up.out = h;
     err = launch_expert<T, 2, kEpiSwiGLU, BT, UP_BF, STAGES, RB>(
-        up, tl.cap * up.feat_tiles, s);
+        up, tl.cap * up.feat_tiles, max_small * up.feat_tiles, s);
     if (err != hipSuccess || w2 == nullptr) return err;      // up product only
 
     GemmParams<T, 1> dn{};
@@ -548,16 +617,17 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
     dn.n_feat = H;
     dn.feat_tiles = (H + DN_BF - 1) / DN_BF;
     dn.table = tl.table;
+    dn.stable = tl.stable;
     dn.table_count = tl.count;
     dn.out = y;
     return launch_expert<T, 1, kEpiStore, BT, DN_BF, STAGES, RB>(
-        dn, tl.cap * dn.feat_tiles, s);
+        dn, tl.cap * dn.feat_tiles, max_small * dn.feat_tiles, s);
 }
 
 }  // namespace
 
 size_t gemm_ws_bytes(long long N, int E) {
-    return 256 + (size_t)tiles_cap(N, E) * sizeof(int4);
+    return 256 + (size_t)(tiles_cap(N, E) + E) * sizeof(int4);
 }
 
 int gate_splits(int dt, int T, int H, int E) {

@@ -197,6 +197,29 @@ def test_grouped_gemm_parity(orc, dt, N, E, H, F):
     assert np.array_equal(host(h_up, dt), h)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_grouped_gemm_tile_boundaries(orc, dt):
+    """Segments on both sides of every tile-size boundary: experts of up to 64 rows take
+    one 64-token tile, larger ones 128-token tiles with a ragged last tile; empty experts
+    take none."""
+    counts = [64, 65, 1, 0, 63, 128, 129, 0, 192, 64, 2, 255, 256, 257, 0, 33]
+    E, H, F = len(counts), 128, 320
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(offsets[-1])
+    rng = np.random.default_rng(64)
+    xd = W._store(rng.standard_normal((N, H)), dt)
+    w1 = W._store(rng.standard_normal((E, F, H)) / np.sqrt(H), dt)
+    w3 = W._store(rng.standard_normal((E, F, H)) / np.sqrt(H), dt)
+    w2 = W._store(rng.standard_normal((E, H, F)) / np.sqrt(F), dt)
+    h_ref, y_ref = orc.grouped_gemm_swiglu(dt, xd, offsets, w1, w3, w2)
+    h, y = ops.moe_grouped_gemm_swiglu(dev(xd, dt), dev(offsets), dev(w1, dt), dev(w3, dt),
+                                       dev(w2, dt))
+    h, y = host(h, dt), host(y, dt)
+    eh, ey = max_abs_rel(h, h_ref, dt), max_abs_rel(y, y_ref, dt)
+    _log(f"gemm tile boundaries {dt}: h err {eh:.2e} y err {ey:.2e}")
+    assert eh <= TOL[dt] and ey <= TOL[dt]
+
+
 # ----------------------------------------------------------------------- whole layer
 
 SMALL_LAYERS = [
