@@ -83,28 +83,14 @@ struct GemmParams {
     int k_slices;           // dense product: k-slices per K split
 };
 
-// Writes 4 consecutive features of one token: fp32 partial logits (per-element bounds; the
-// top-k step adds the bias), or the storage type (n_feat is a multiple of 64 there, so a
-// run never straddles the end).
-template <typename T, int NB, int EPI>
-__device__ __forceinline__ void store_run(const GemmParams<T, NB>& p, int tok, int feat,
-                                          const float (&r)[4]) {
-    if constexpr (EPI == kEpiLogits) {
-        float* o = reinterpret_cast<float*>(p.out) + (size_t)tok * p.n_feat;
+// Writes 4 consecutive fp32 partial logits of one token (per-element bounds: E need not be
+// a multiple of 4; the top-k step adds the bias).
+__device__ __forceinline__ void store_logits(float* out, int n_feat, int tok, int feat,
+                                             const float (&r)[4]) {
+    float* o = out + (size_t)tok * n_feat;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            if (feat + v < p.n_feat) o[feat + v] = r[v];
-    } else if constexpr (sizeof(T) == 4) {
-        if (feat >= p.n_feat) return;
-        float* o = reinterpret_cast<float*>(p.out) + (size_t)tok * p.n_feat + feat;
-        *reinterpret_cast<float4*>(o) = make_float4(r[0], r[1], r[2], r[3]);
-    } else {
-        if (feat >= p.n_feat) return;
-        uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + (size_t)tok * p.n_feat + feat;
-        const uint32_t lo = f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
-        const uint32_t hi = f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
-        *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
-    }
+    for (int v = 0; v < 4; ++v)
+        if (feat + v < n_feat) o[feat + v] = r[v];
 }
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
@@ -267,6 +253,7 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
 #undef MOE_ISSUE
         // redundant copies may still be landing; the workgroup's LDS must be quiet first
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));           // vmcnt(0)
+        if constexpr (EPI != kEpiLogits) __builtin_amdgcn_s_barrier();   // ring free: staging
         return;
     }
 
@@ -353,24 +340,70 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
 #undef MOE_MFMAS
 
     // ---- epilogue: lane holds one token and, per 32-feature tile, 4 runs of 4 features ----
+    if constexpr (EPI == kEpiLogits) {
 #pragma unroll
-    for (int i = 0; i < FT; ++i) {
+        for (int i = 0; i < FT; ++i) {
 #pragma unroll
-        for (int j = 0; j < TT; ++j) {
-            const int tok = row0 + wt * (BT / 2) + j * 32 + l32;
-            if (tok >= row_end) continue;
+            for (int j = 0; j < TT; ++j) {
+                const int tok = row0 + wt * (BT / 2) + j * 32 + l32;
+                if (tok >= row_end) continue;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int feat = f0 + wf * (BF / 2) + i * 32 + 8 * g + 4 * lhalf;
-                float r[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float a = acc[0][i][j][4 * g + v];
-                    if constexpr (EPI == kEpiSwiGLU) r[v] = silu(a) * acc[NB - 1][i][j][4 * g + v];
-                    else r[v] = a;
+                for (int g = 0; g < 4; ++g) {
+                    const float(&a)[16] = reinterpret_cast<const float(&)[16]>(acc[0][i][j]);
+                    const float r[4] = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+                    store_logits(static_cast<float*>(p.out), p.n_feat, tok,
+                                 f0 + wf * (BF / 2) + i * 32 + 8 * g + 4 * lhalf, r);
                 }
-                store_run<T, NB, EPI>(p, tok, feat, r);
             }
+        }
+    } else {
+        // Expert outputs go through LDS: each wave writes its (BT/2) x (BF/2) block into a
+        // region of its own in the MFMA layout, then reads it back by rows so every store
+        // instruction writes whole row segments (a direct store from the MFMA layout touches
+        // 32 rows per instruction, 8 or 16 bytes each).  The barrier (the loaders' last,
+        // after their transfers have landed) frees the ring for this.
+        constexpr int kRowOut = (BF / 2) * (int)sizeof(T);     // bytes of one token's block row
+        constexpr int kPitch = kRowOut + 16;                   // +16: rows 16 apart share banks
+        constexpr int kCpr = kRowOut / 16;                     // 16-byte chunks per row
+        constexpr int kOutChunks = (BT / 2) * kCpr;
+        static_assert(4 * (BT / 2) * kPitch <= S * kStageBytes && kOutChunks % 64 == 0, "staging");
+        __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (3 << 14));   // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        char* stg = lds + wave * (BT / 2) * kPitch;
+#pragma unroll
+        for (int i = 0; i < FT; ++i) {
+#pragma unroll
+            for (int j = 0; j < TT; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float r[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float a = acc[0][i][j][4 * g + v];
+                        if constexpr (EPI == kEpiSwiGLU) r[v] = silu(a) * acc[NB - 1][i][j][4 * g + v];
+                        else r[v] = a;
+                    }
+                    char* dst = stg + (j * 32 + l32) * kPitch + (i * 32 + 8 * g + 4 * lhalf) * (int)sizeof(T);
+                    if constexpr (sizeof(T) == 4) {
+                        *reinterpret_cast<float4*>(dst) = make_float4(r[0], r[1], r[2], r[3]);
+                    } else {
+                        *reinterpret_cast<uint2*>(dst) =
+                            make_uint2(f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16),
+                                       f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16));
+                    }
+                }
+            }
+        }
+        const int tok0 = row0 + wt * (BT / 2), feat0 = f0 + wf * (BF / 2);
+        T* out = static_cast<T*>(p.out);
+#pragma unroll
+        for (int k = 0; k < kOutChunks / 64; ++k) {
+            const int c = lane + 64 * k;
+            const int r = c / kCpr, cc = c - r * kCpr;
+            const int tok = tok0 + r, feat = feat0 + cc * (16 / (int)sizeof(T));
+            const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kPitch + cc * 16);
+            if (tok < row_end && feat < p.n_feat)
+                *reinterpret_cast<uint4*>(out + (size_t)tok * p.n_feat + feat) = v;
         }
     }
 }
