@@ -170,7 +170,7 @@ def _segments(rng, E, N, empties=True):
 
 GEMM_SHAPES = [  # (N, E, H, F)
     (1, 1, 64, 64), (37, 3, 64, 128), (600, 12, 256, 192), (1000, 5, 192, 320),
-    (700, 1, 128, 256), (2000, 40, 128, 128)]
+    (700, 1, 128, 256), (2000, 40, 128, 128), (3000, 1024, 64, 128)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -226,6 +226,8 @@ SMALL_LAYERS = [
     W.CONFIGS["tiny_f32"],
     W.LayerConfig("small_bf16", T=300, H=256, E=16, F=192, k=4, dtype="bf16", bias=("zipf", 1.2)),
     W.LayerConfig("small_f32", T=200, H=128, E=24, F=320, k=6, dtype="f32", bias=("zipf", 1.0)),
+    # the most experts the ABI takes: nearly every expert has a handful of rows
+    W.LayerConfig("wide_bf16", T=256, H=128, E=1024, F=128, k=8, dtype="bf16", bias=("zipf", 1.2)),
 ]
 
 
