@@ -15,7 +15,7 @@
 namespace moe {
 namespace {
 
-constexpr int kSegChunks = 16;
+constexpr int kSegChunks = 8;
 constexpr int kSeg = kWave * kSegChunks;  // routing entries per wave
 constexpr int kWavesPerBlock = 4;
 constexpr int kEMax = 1024;
@@ -66,18 +66,26 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void pft_hist_kernel(
     }
 }
 
-// One workgroup: per-expert exclusive prefix over segments, counts, offsets, and the
-// absolute base position of every (segment, expert).
+// One workgroup: per-expert exclusive prefix over segments (the position of a segment's
+// first entry of expert e within e's rows), counts and offsets.  Segment counts are read
+// kBatch at a time before any is written back, so their latencies overlap.
 __global__ __launch_bounds__(kEMax) void pft_scan_kernel(int E, int nseg, int32_t* counts,
                                                          int32_t* offsets, PftWs w) {
+    constexpr int kBatch = 16;
     __shared__ int scan[2][kEMax];
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-        for (int s = 0; s < nseg; ++s) {
-            const int v = w.hist[(size_t)s * E + e];
-            w.hist[(size_t)s * E + e] = run;
-            run += v;
+        for (int s0 = 0; s0 < nseg; s0 += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b)
+                v[b] = s0 + b < nseg ? w.hist[(size_t)(s0 + b) * E + e] : 0;
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                if (s0 + b < nseg) w.hist[(size_t)(s0 + b) * E + e] = run;
+                run += v[b];
+            }
         }
         counts[e] = run;
     }
@@ -95,7 +103,6 @@ __global__ __launch_bounds__(kEMax) void pft_scan_kernel(int E, int nseg, int32_
     if (e < E) {
         offsets[e] = base;
         if (e == E - 1) offsets[E] = incl;
-        for (int s = 0; s < nseg; ++s) w.hist[(size_t)s * E + e] += base;
     }
     if (e == 0) {
         int bad = 0;
@@ -106,12 +113,13 @@ __global__ __launch_bounds__(kEMax) void pft_scan_kernel(int E, int nseg, int32_
 
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void pft_scatter_kernel(
     const int32_t* __restrict__ te, long long N, int k, int E, int nseg, int nbits, PftWs w,
-    int32_t* __restrict__ token_ids, int32_t* __restrict__ expert_ids, int32_t* __restrict__ dest_pos) {
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ token_ids,
+    int32_t* __restrict__ expert_ids, int32_t* __restrict__ dest_pos) {
     __shared__ int next[kWavesPerBlock][kEMax];
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int seg = blockIdx.x * kWavesPerBlock + wv;
     if (seg >= nseg) return;  // whole wave; the waves never meet at a block barrier
-    for (int e = lane; e < E; e += kWave) next[wv][e] = w.hist[(size_t)seg * E + e];
+    for (int e = lane; e < E; e += kWave) next[wv][e] = offsets[e] + w.hist[(size_t)seg * E + e];
     wave_fence();
     const uint64_t below = lanemask_lt();
     for (int c = 0; c < kSegChunks; ++c) {
@@ -166,7 +174,7 @@ hipError_t launch_pft(int T, int k, int E, const int32_t* te, int32_t* counts, i
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || nseg == 0) return err;
     hipLaunchKernelGGL(pft_scatter_kernel, dim3(blocks), dim3(kWave * kWavesPerBlock), 0, s, te, N,
-                       k, E, nseg, nbits, w, token_ids, expert_ids, dest_pos);
+                       k, E, nseg, nbits, w, offsets, token_ids, expert_ids, dest_pos);
     return hipGetLastError();
 }
 
