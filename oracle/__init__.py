@@ -1,4 +1,4 @@
-"""CPU oracle for the MoE layer forward -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the MoE layer forward and backward -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
 may import this package.  The product path (``gemm_gate_softmax_amd``) never imports it
@@ -51,10 +51,17 @@ def lib() -> ctypes.CDLL:
         L.oracle_grouped_gemm_swiglu.argtypes = [i32] * 5 + [vp] * 7
         L.oracle_combine.argtypes = [i32] * 4 + [vp] * 4
         L.oracle_layer_forward.argtypes = [i32] * 7 + [vp] * 8
+        L.oracle_combine_backward.argtypes = [i32] * 4 + [vp] * 6
+        L.oracle_expert_backward.argtypes = [i32] * 5 + [vp] * 12
+        L.oracle_dispatch_backward.argtypes = [i32] * 3 + [vp] * 3
+        L.oracle_gate_backward.argtypes = [i32] * 6 + [vp] * 9
+        L.oracle_layer_backward.argtypes = [i32] * 7 + [vp] * 14
         L.oracle_round_bf16.argtypes = [vp, vp, lng]
         L.oracle_num_threads.argtypes = []
         for f in ("oracle_gate_topk", "oracle_pft_build", "oracle_dispatch",
                   "oracle_grouped_gemm_swiglu", "oracle_combine", "oracle_layer_forward",
+                  "oracle_combine_backward", "oracle_expert_backward",
+                  "oracle_dispatch_backward", "oracle_gate_backward", "oracle_layer_backward",
                   "oracle_num_threads"):
             getattr(L, f).restype = ctypes.c_int
         L.oracle_round_bf16.restype = None
@@ -174,3 +181,89 @@ def layer_forward(dt, x, wg, bias, w1, w3, w2, k, stage_seconds=False, routing="
                                       _p(b), _p(w1), _p(w3), _p(w2), _p(out), _p(secs)),
            "layer_forward")
     return (out, secs) if stage_seconds else out
+
+
+# ----------------------------------------------------------------------------- backward
+# Gradients (double) of the loss sum(dout * out) with the expert picks held fixed; see the
+# backward section of oracle.c for the formulas and the readings behind them.
+
+def combine_backward(dt, dout, y, dest_pos, top_weights):
+    """Returns (dy [N,H] f64, dw [T,k] f64)."""
+    st = _storage(dt)
+    dout, y = _c(dout, st), _c(y, st)
+    dp = _c(dest_pos, np.int32)
+    tw = _c(top_weights, np.float32)
+    T, k = dp.shape
+    H = y.shape[1]
+    dy = np.empty((T * k, H), np.float64)
+    dw = np.empty((T, k), np.float64)
+    _check(lib().oracle_combine_backward(_DT[dt], T, k, H, _p(dout), _p(y), _p(dp), _p(tw),
+                                         _p(dy), _p(dw)), "combine_backward")
+    return dy, dw
+
+
+def expert_backward(dt, xd, offsets, w1, w3, w2, dy, h=None):
+    """Returns dict(dxd [N,H], dw1 [E,F,H], dw3 [E,F,H], dw2 [E,H,F]), all f64."""
+    st = _storage(dt)
+    xd = _c(xd, st)
+    off = _c(offsets, np.int32)
+    w1, w3, w2 = _c(w1, st), _c(w3, st), _c(w2, st)
+    h = None if h is None else _c(h, st)
+    dy = _c(dy, np.float64)
+    N, H = xd.shape
+    E, F = w1.shape[0], w1.shape[1]
+    out = dict(dxd=np.empty((N, H)), dw1=np.empty((E, F, H)), dw3=np.empty((E, F, H)),
+               dw2=np.empty((E, H, F)))
+    _check(lib().oracle_expert_backward(_DT[dt], N, E, H, F, _p(xd), _p(off), _p(w1), _p(w3),
+                                        _p(w2), _p(h), _p(dy), _p(out["dxd"]), _p(out["dw1"]),
+                                        _p(out["dw3"]), _p(out["dw2"])), "expert_backward")
+    return out
+
+
+def dispatch_backward(dxd, dest_pos):
+    """Returns dx [T,H] f64: the sum of each token's k buffer-row gradients."""
+    dxd = _c(dxd, np.float64)
+    dp = _c(dest_pos, np.int32)
+    T, k = dp.shape
+    H = dxd.shape[1]
+    dx = np.empty((T, H), np.float64)
+    _check(lib().oracle_dispatch_backward(T, k, H, _p(dxd), _p(dp), _p(dx)), "dispatch_backward")
+    return dx
+
+
+def gate_backward(dt, x, wg, bias, top_experts, dw, routing="softmax", dx=None):
+    """Returns dict(dx [T,H] (dx + the gate's part when dx is given), dwg [E,H], dbias [E],
+    dl [T,k]), all f64."""
+    st = _storage(dt)
+    x, wg = _c(x, st), _c(wg, st)
+    b = None if bias is None else _c(bias, np.float32)
+    te = _c(top_experts, np.int32)
+    dw = _c(dw, np.float64)
+    T, H = x.shape
+    E = wg.shape[0]
+    k = te.shape[1]
+    out = dict(dx=np.zeros((T, H)) if dx is None else np.array(dx, np.float64, copy=True),
+               dwg=np.empty((E, H)), dbias=np.empty(E), dl=np.empty((T, k)))
+    _check(lib().oracle_gate_backward(_DT[dt], T, H, E, k, ROUTING[routing], _p(x), _p(wg), _p(b),
+                                      _p(te), _p(dw), _p(out["dx"]), _p(out["dwg"]),
+                                      _p(out["dbias"]), _p(out["dl"])), "gate_backward")
+    return out
+
+
+def layer_backward(dt, x, wg, bias, w1, w3, w2, k, dout, routing="softmax"):
+    """Returns dict(dx, dwg, dbias, dw1, dw3, dw2, dtw), all f64."""
+    st = _storage(dt)
+    x, wg, dout = _c(x, st), _c(wg, st), _c(dout, st)
+    w1, w3, w2 = _c(w1, st), _c(w3, st), _c(w2, st)
+    b = None if bias is None else _c(bias, np.float32)
+    T, H = x.shape
+    E, F = w1.shape[0], w1.shape[1]
+    out = dict(dx=np.empty((T, H)), dwg=np.empty((E, H)), dbias=np.empty(E),
+               dw1=np.empty((E, F, H)), dw3=np.empty((E, F, H)), dw2=np.empty((E, H, F)),
+               dtw=np.empty((T, k)))
+    _check(lib().oracle_layer_backward(_DT[dt], T, H, E, F, k, ROUTING[routing], _p(x), _p(wg),
+                                       _p(b), _p(w1), _p(w3), _p(w2), _p(dout), _p(out["dx"]),
+                                       _p(out["dwg"]), _p(out["dbias"]), _p(out["dw1"]),
+                                       _p(out["dw3"]), _p(out["dw2"]), _p(out["dtw"])),
+           "layer_backward")
+    return out

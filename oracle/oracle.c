@@ -1,7 +1,7 @@
 /*
  * oracle.c -- plain, slow, obviously-correct CPU reference for the forward pass of one
  * expert-specialised MoE layer (top-k softmax gate, padding-free token buffers,
- * dispatch, SwiGLU experts, weighted combine).
+ * dispatch, SwiGLU experts, weighted combine) and its backward.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or load this
  * file: only the test suite, the package smoke check and the benchmark's CPU-baseline
@@ -37,7 +37,10 @@
  * inputs, closed-form weights, brute-force buffer positions and the buffer invariants,
  * dispatch+combine round trip, the dense capacity-padded (GShard-style) formulation,
  * the E=1/k=1 dense SwiGLU FFN, identical experts, pure-Python per-row loops, and the
- * bf16 rounding of a library conversion.  Every function below is pinned by at least one.
+ * bf16 rounding of a library conversion; for the backward, central finite differences
+ * of the forward, an independent float64 autograd of the same mixture, the zero-sum of
+ * softmax-routing logit gradients and linearity in dout.  Every function below is pinned
+ * by at least one.
  */
 #define _POSIX_C_SOURCE 200809L
 #include <math.h>
@@ -373,6 +376,269 @@ int oracle_layer_forward(int dt, int T, int H, int E, int F, int k, int routing,
 done:
     free(te); free(tw); free(counts); free(offsets); free(tok); free(eid); free(dpos);
     free(xd); free(y);
+    return rc;
+}
+
+/* ------------------------------------------------------------------- backward -- */
+/*
+ * Gradients of the layer above for a loss L with dL/dout = dout, the expert picks held
+ * fixed (top-k selection is piecewise constant in the logits).  The pages name training
+ * as the purpose of the layer ([XMOE] 训练流程 steps 4-7 follow the forward with the
+ * backward and the weight update; [FDMOE] section 10 lists training as future work) but
+ * give no backward formulas; these are the derivatives of the forward as defined above,
+ * with the reading that a value rounded to storage (h, y, the fp32 routing weights) is
+ * used as stored where the forward uses it, and differentiated as if unrounded.  All
+ * gradient arithmetic is in double; gradients are returned as double arrays.
+ */
+
+/*
+ * Combine backward: out[t] = sum_j w[t][j] * y[p] with p = dest_pos[t][j], so
+ *   dy[p][c]   = w[t][j] * dout[t][c]
+ *   dw[t][j]   = sum_c dout[t][c] * y[p][c]
+ * dy [N][H] and dw [T][k] are written (double).
+ */
+int oracle_combine_backward(int dt, int T, int k, int H, const void *dout, const void *y,
+                            const int32_t *dest_pos, const float *top_weights, double *dy,
+                            double *dw) {
+    if (!valid_dtype(dt) || T < 0 || k < 1 || H <= 0) return OR_EINVAL;
+    long N = (long)T * k;
+    for (long i = 0; i < N; ++i)
+        if (dest_pos[i] < 0 || dest_pos[i] >= N) return OR_ERANGE;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            size_t i = (size_t)t * k + j, p = (size_t)dest_pos[i];
+            double w = (double)top_weights[i], d = 0.0;
+            for (int c = 0; c < H; ++c) {
+                double g = load_elem(dt, dout, (size_t)t * H + c);
+                dy[p * H + c] = w * g;
+                d += g * load_elem(dt, y, p * H + c);
+            }
+            dw[i] = d;
+        }
+    }
+    return OR_OK;
+}
+
+/*
+ * Expert backward for rows p of expert e (segments as in the forward), with
+ * a = xd.W1[e]^T, g = xd.W3[e]^T (unrounded), h the forward's stored h:
+ *   dh[f]        = sum_c dy[p][c] * W2[e][c][f]
+ *   da[f]        = dh[f] * g[f] * silu'(a[f]),  silu'(a) = s * (1 + a * (1 - s)),  s = 1/(1+e^-a)
+ *   dg[f]        = dh[f] * silu(a[f])
+ *   dxd[p][c]    = sum_f da[f] * W1[e][f][c] + dg[f] * W3[e][f][c]
+ *   dW2[e][c][f] = sum_p dy[p][c] * h[p][f]
+ *   dW1[e][f][c] = sum_p da[f] * xd[p][c],   dW3[e][f][c] = sum_p dg[f] * xd[p][c]
+ * h may be NULL: it is then recomputed and rounded to storage as the forward does.
+ * dxd [N][H], dw1 and dw3 [E][F][H], dw2 [E][H][F] are written (double).
+ */
+int oracle_expert_backward(int dt, int N, int E, int H, int F, const void *xd,
+                           const int32_t *offsets, const void *w1, const void *w3,
+                           const void *w2, const void *h, const double *dy, double *dxd,
+                           double *dw1, double *dw3, double *dw2) {
+    if (!valid_dtype(dt) || N < 0 || E < 1 || H <= 0 || F <= 0) return OR_EINVAL;
+    if (offsets[0] != 0 || offsets[E] != N) return OR_EINVAL;
+    for (int e = 0; e < E; ++e)
+        if (offsets[e + 1] < offsets[e]) return OR_EINVAL;
+    size_t es = elem_size(dt);
+    memset(dw1, 0, sizeof(double) * (size_t)E * F * H);
+    memset(dw3, 0, sizeof(double) * (size_t)E * F * H);
+    memset(dw2, 0, sizeof(double) * (size_t)E * H * F);
+    double *da = (double *)malloc(sizeof(double) * (size_t)(N ? N : 1) * F);
+    double *dg = (double *)malloc(sizeof(double) * (size_t)(N ? N : 1) * F);
+    char *hs = (char *)malloc((size_t)(N ? N : 1) * F * es);   /* stored h, [N][F] */
+    if (!da || !dg || !hs) { free(da); free(dg); free(hs); return OR_ENOMEM; }
+    for (int e = 0; e < E; ++e) {
+        size_t wb1 = (size_t)e * F * H, wb2 = (size_t)e * H * F;
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int p = offsets[e]; p < offsets[e + 1]; ++p) {
+            for (int f = 0; f < F; ++f) {
+                double a = 0.0, g = 0.0, dh = 0.0;
+                for (int c = 0; c < H; ++c) {
+                    double xv = load_elem(dt, xd, (size_t)p * H + c);
+                    a += xv * load_elem(dt, w1, wb1 + (size_t)f * H + c);
+                    g += xv * load_elem(dt, w3, wb1 + (size_t)f * H + c);
+                    dh += dy[(size_t)p * H + c] * load_elem(dt, w2, wb2 + (size_t)c * F + f);
+                }
+                double sg = 1.0 / (1.0 + exp(-a));
+                da[(size_t)p * F + f] = dh * g * sg * (1.0 + a * (1.0 - sg));
+                dg[(size_t)p * F + f] = dh * a * sg;
+                if (h) memcpy(hs + ((size_t)p * F + f) * es, (const char *)h + ((size_t)p * F + f) * es, es);
+                else store_elem(dt, hs, (size_t)p * F + f, a * sg * g);
+            }
+            for (int c = 0; c < H; ++c) {
+                double s = 0.0;
+                for (int f = 0; f < F; ++f)
+                    s += da[(size_t)p * F + f] * load_elem(dt, w1, wb1 + (size_t)f * H + c) +
+                         dg[(size_t)p * F + f] * load_elem(dt, w3, wb1 + (size_t)f * H + c);
+                dxd[(size_t)p * H + c] = s;
+            }
+        }
+        /* weight gradients: sums over the expert's rows in ascending p */
+#pragma omp parallel for schedule(static)
+        for (int f = 0; f < F; ++f) {
+            for (int p = offsets[e]; p < offsets[e + 1]; ++p) {
+                double a_ = da[(size_t)p * F + f], g_ = dg[(size_t)p * F + f];
+                double hv = load_elem(dt, hs, (size_t)p * F + f);
+                for (int c = 0; c < H; ++c) {
+                    double xv = load_elem(dt, xd, (size_t)p * H + c);
+                    dw1[wb1 + (size_t)f * H + c] += a_ * xv;
+                    dw3[wb1 + (size_t)f * H + c] += g_ * xv;
+                    dw2[wb2 + (size_t)c * F + f] += dy[(size_t)p * H + c] * hv;
+                }
+            }
+        }
+    }
+    free(da); free(dg); free(hs);
+    return OR_OK;
+}
+
+/* Dispatch backward: xd[p] = x[t] for every slot, so dx[t][c] = sum_j dxd[dest_pos[t][j]][c]. */
+int oracle_dispatch_backward(int T, int k, int H, const double *dxd, const int32_t *dest_pos,
+                             double *dx) {
+    if (T < 0 || k < 1 || H <= 0) return OR_EINVAL;
+    long N = (long)T * k;
+    for (long i = 0; i < N; ++i)
+        if (dest_pos[i] < 0 || dest_pos[i] >= N) return OR_ERANGE;
+    for (int t = 0; t < T; ++t)
+        for (int c = 0; c < H; ++c) {
+            double s = 0.0;
+            for (int j = 0; j < k; ++j) s += dxd[(size_t)dest_pos[(size_t)t * k + j] * H + c];
+            dx[(size_t)t * H + c] = s;
+        }
+    return OR_OK;
+}
+
+/*
+ * Gate backward.  The picks are held fixed and the weights of token t depend only on its
+ * picked logits l_j (the fp32 logits of the forward, differentiated as exact):
+ *   routing 0: w_j = exp(l_j) / sum_i exp(l_i)  (the all-expert softmax normaliser cancels)
+ *              dl_j = w_j * (dw_j - sum_i w_i dw_i)
+ *   routing 1: w_j = s_j / S, s = sigmoid(l), S = sum_i s_i
+ *              dl_j = (dw_j - sum_i w_i dw_i) / S * s_j * (1 - s_j)
+ * with w in double before its fp32 rounding.  Unpicked logits get no gradient.  Then, as
+ * logit = x.Wg^T + bias:
+ *   dx[t][h] += sum_j dl_j Wg[e_j][h],  dWg[e][h] = sum_t dl_te x[t][h],  dbias[e] = sum_t dl_te
+ * dx is accumulated into (the caller initialises it); dwg [E][H] and dbias [E] are written.
+ * dl [T][k] (double) is written when not NULL.
+ */
+int oracle_gate_backward(int dt, int T, int H, int E, int k, int routing, const void *x,
+                         const void *wg, const float *bias, const int32_t *top_experts,
+                         const double *dw, double *dx, double *dwg, double *dbias, double *dl) {
+    if (!valid_dtype(dt) || T < 0 || H <= 0 || E <= 0 || k < 1 || k > E) return OR_EINVAL;
+    if (routing != 0 && routing != 1) return OR_EINVAL;
+    for (long i = 0; i < (long)T * k; ++i)
+        if (top_experts[i] < 0 || top_experts[i] >= E) return OR_ERANGE;
+    memset(dwg, 0, sizeof(double) * (size_t)E * H);
+    memset(dbias, 0, sizeof(double) * (size_t)E);
+    double *dlt = (double *)malloc(sizeof(double) * (size_t)(T ? T : 1) * k);
+    if (!dlt) return OR_ENOMEM;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        double l[64], w[64], z = 0.0, S = 0.0, m = -INFINITY;   /* k <= 64 */
+        for (int j = 0; j < k; ++j) {
+            int e = top_experts[(size_t)t * k + j];
+            double s = 0.0;
+            for (int h = 0; h < H; ++h)
+                s += load_elem(dt, x, (size_t)t * H + h) * load_elem(dt, wg, (size_t)e * H + h);
+            if (bias) s += (double)bias[e];
+            l[j] = (double)(float)s;
+            if (l[j] > m) m = l[j];
+        }
+        for (int j = 0; j < k; ++j) {
+            w[j] = routing == 0 ? exp(l[j] - m) : 1.0 / (1.0 + exp(-l[j]));
+            z += w[j];
+        }
+        S = z;
+        double wdw = 0.0;
+        for (int j = 0; j < k; ++j) {
+            w[j] /= z;
+            wdw += w[j] * dw[(size_t)t * k + j];
+        }
+        for (int j = 0; j < k; ++j) {
+            double r = dw[(size_t)t * k + j] - wdw;
+            if (routing == 0) {
+                dlt[(size_t)t * k + j] = w[j] * r;
+            } else {
+                double sj = w[j] * S;              /* sigmoid(l_j) */
+                dlt[(size_t)t * k + j] = r / S * sj * (1.0 - sj);
+            }
+        }
+        for (int h = 0; h < H; ++h) {
+            double s = 0.0;
+            for (int j = 0; j < k; ++j)
+                s += dlt[(size_t)t * k + j] * load_elem(dt, wg, (size_t)top_experts[(size_t)t * k + j] * H + h);
+            dx[(size_t)t * H + h] += s;
+        }
+    }
+    /* dWg and dbias: sums over tokens in ascending t */
+#pragma omp parallel for schedule(static)
+    for (int e = 0; e < E; ++e) {
+        for (int t = 0; t < T; ++t)
+            for (int j = 0; j < k; ++j) {
+                if (top_experts[(size_t)t * k + j] != e) continue;
+                double d = dlt[(size_t)t * k + j];
+                dbias[e] += d;
+                for (int h = 0; h < H; ++h) dwg[(size_t)e * H + h] += d * load_elem(dt, x, (size_t)t * H + h);
+            }
+    }
+    if (dl) memcpy(dl, dlt, sizeof(double) * (size_t)T * k);
+    free(dlt);
+    return OR_OK;
+}
+
+/*
+ * The whole backward: the forward's gate, buffers, dispatch and experts are run again
+ * (h and y as the forward stores them), then combine, expert, dispatch and gate
+ * backward in that order.  dx [T][H], dwg [E][H], dbias [E], dw1 and dw3 [E][F][H],
+ * dw2 [E][H][F] are written (double); dtw [T][k] (the routing-weight gradient) too when
+ * not NULL.
+ */
+int oracle_layer_backward(int dt, int T, int H, int E, int F, int k, int routing, const void *x,
+                          const void *wg, const float *bias, const void *w1, const void *w3,
+                          const void *w2, const void *dout, double *dx, double *dwg,
+                          double *dbias, double *dw1, double *dw3, double *dw2, double *dtw) {
+    if (!valid_dtype(dt) || T < 0 || H <= 0 || E < 1 || F <= 0 || k < 1 || k > E)
+        return OR_EINVAL;
+    if (routing != 0 && routing != 1) return OR_EINVAL;
+    long N = (long)T * k;
+    size_t es = elem_size(dt), n1 = (size_t)(N ? N : 1);
+    int32_t *te = (int32_t *)malloc(sizeof(int32_t) * n1);
+    float *tw = (float *)malloc(sizeof(float) * n1);
+    int32_t *counts = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    int32_t *offsets = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
+    int32_t *tok = (int32_t *)malloc(sizeof(int32_t) * n1);
+    int32_t *eid = (int32_t *)malloc(sizeof(int32_t) * n1);
+    int32_t *dpos = (int32_t *)malloc(sizeof(int32_t) * n1);
+    void *xd = malloc(n1 * H * es), *h = malloc(n1 * F * es), *y = malloc(n1 * H * es);
+    double *dy = (double *)malloc(sizeof(double) * n1 * H);
+    double *dxd = (double *)malloc(sizeof(double) * n1 * H);
+    double *dwt = (double *)malloc(sizeof(double) * n1);
+    int rc = OR_ENOMEM;
+    if (!te || !tw || !counts || !offsets || !tok || !eid || !dpos || !xd || !h || !y || !dy ||
+        !dxd || !dwt)
+        goto done;
+    rc = oracle_gate_topk(dt, T, H, E, k, routing, x, wg, bias, te, tw, NULL, NULL);
+    if (rc) goto done;
+    rc = oracle_pft_build(T, k, E, te, counts, offsets, tok, eid, dpos);
+    if (rc) goto done;
+    rc = oracle_dispatch(dt, T, k, H, x, dpos, xd);
+    if (rc) goto done;
+    rc = oracle_grouped_gemm_swiglu(dt, (int)N, E, H, F, xd, offsets, w1, w3, w2, h, y);
+    if (rc) goto done;
+    rc = oracle_combine_backward(dt, T, k, H, dout, y, dpos, tw, dy, dwt);
+    if (rc) goto done;
+    rc = oracle_expert_backward(dt, (int)N, E, H, F, xd, offsets, w1, w3, w2, h, dy, dxd, dw1,
+                                dw3, dw2);
+    if (rc) goto done;
+    rc = oracle_dispatch_backward(T, k, H, dxd, dpos, dx);
+    if (rc) goto done;
+    rc = oracle_gate_backward(dt, T, H, E, k, routing, x, wg, bias, te, dwt, dx, dwg, dbias, NULL);
+    if (rc) goto done;
+    if (dtw) memcpy(dtw, dwt, sizeof(double) * (size_t)N);
+done:
+    free(te); free(tw); free(counts); free(offsets); free(tok); free(eid); free(dpos);
+    free(xd); free(h); free(y); free(dy); free(dxd); free(dwt);
     return rc;
 }
 
