@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.hip", "gemm.hip", "gate.hip", "pft.hip", "move.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gate.hip", "pft.hip", "move.hip", "backward.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 vector ops are switched off for all device code (the compiler otherwise

@@ -69,6 +69,9 @@ MOE_API size_t moe_workspace_bytes(int kind, int T, int H, int E, int F, int k, 
         case MOE_WS_PFT: return pft_ws(T, k, E);
         case MOE_WS_GEMM: return gemm_ws((long long)T * k, E);
         case MOE_WS_LAYER: return pft_ws(T, k, E) + gate_ws(dt, T, H, E) + gemm_ws((long long)T * k, E);
+        case MOE_WS_BACKWARD:
+            if (check_dim(F) != MOE_OK) return 0;
+            return round_up(moe::backward_ws_bytes(dt, T, H, E, F, k));
         default: return 0;
     }
 }
@@ -195,4 +198,35 @@ MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int 
                                                          ws_gemm, s)));
     }
     return launched(moe::launch_combine(dt, T, k, H, b->y, b->dest_pos, b->top_weights, out, s));
+}
+
+MOE_API moe_status_t moe_layer_backward(moe_dtype_t dt, int T, int H, int E, int F, int k,
+                                        moe_routing_t routing, const void* x, const void* wg,
+                                        const float* bias, const void* w1, const void* w3,
+                                        const void* w2, const moe_layer_bufs* fwd,
+                                        const void* dout, void* dx, void* dwg, float* dbias,
+                                        void* dw1, void* dw3, void* dw2, float* dtop_weights,
+                                        void* ws, size_t ws_bytes, void* stream) {
+    if (!valid_dt(dt) || !valid_routing(routing) || !fwd) return MOE_ERR_INVALID_VALUE;
+    MOE_TRY(check_route(T, E, k));
+    MOE_TRY(check_dim(H));
+    MOE_TRY(check_dim(F));
+    if (T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({x, wg, w1, w3, w2, dout, dx, dwg, dbias, dw1, dw3, dw2, ws,
+                        fwd->top_experts, fwd->top_weights, fwd->counts, fwd->offsets,
+                        fwd->token_ids, fwd->dest_pos, fwd->h, fwd->y}));
+    if (fwd->xd && !aligned16(fwd->xd)) return MOE_ERR_MISALIGNED;
+    if (bias && !aligned16(bias)) return MOE_ERR_MISALIGNED;
+    if (dtop_weights && !aligned16(dtop_weights)) return MOE_ERR_MISALIGNED;
+    if (ws_bytes < round_up(moe::backward_ws_bytes(dt, T, H, E, F, k)))
+        return MOE_ERR_WORKSPACE_TOO_SMALL;
+    moe::BwdParams b{};
+    b.dt = dt; b.T = T; b.H = H; b.E = E; b.F = F; b.k = k; b.routing = routing;
+    b.x = x; b.wg = wg; b.bias = bias; b.w1 = w1; b.w3 = w3; b.w2 = w2;
+    b.top_experts = fwd->top_experts; b.top_weights = fwd->top_weights;
+    b.counts = fwd->counts; b.offsets = fwd->offsets; b.token_ids = fwd->token_ids;
+    b.dest_pos = fwd->dest_pos; b.xd = fwd->xd; b.h = fwd->h; b.y = fwd->y; b.dout = dout;
+    b.dx = dx; b.dwg = dwg; b.dbias = dbias; b.dw1 = dw1; b.dw3 = dw3; b.dw2 = dw2;
+    b.dtw = dtop_weights; b.ws = ws;
+    return launched(moe::launch_layer_backward(b, as_stream(stream)));
 }

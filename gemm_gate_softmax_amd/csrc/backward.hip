@@ -1,0 +1,475 @@
+// backward.hip -- the layer backward: gradients of the loss with dL/dout given, the expert
+// picks held fixed (selection is piecewise constant in the logits).
+//
+// The pages present the layer as part of a training system (X-MoE review, section 三,
+// 训练流程: the forward is followed by the backward and the weight update; FlashDMoE blog,
+// section 10: training as future work) without backward formulas; the gradients here are
+// the derivatives of the forward of this library:
+//   combine:  dy[p] = w[t][j] dout[t],  dw[t][j] = <dout[t], y[p]>              (p = dest_pos[t][j])
+//   experts:  dh = dy W2[e],  da = dh g silu'(a),  dg = dh silu(a),  dxd = da W1[e] + dg W3[e]
+//             dW2[e] = dy_e^T h_e,  dW1[e] = da_e^T xd_e,  dW3[e] = dg_e^T xd_e
+//   dispatch: dx[t] = sum_j dxd[p]
+//   gate:     dl from dw through the routing weights of the picked logits (softmax over the
+//             picks, or normalised sigmoids), dx[t] += sum_j dl_j Wg[e_j],
+//             dWg = DL^T x, dbias = column sums of DL (DL [T][E] holds dl at the picks)
+// Every product runs on the NT tile GEMM of gemm.hip: weights are transposed per active
+// expert, and the weight gradients read activations transposed into per-expert column
+// blocks aligned to 64 and zero padded, so each expert's gradient is one GEMM over its own
+// K range.  All accumulation is fp32; every gradient tensor is rounded once to its storage
+// type (dbias, dw and dl stay fp32).  Deterministic: no atomics.
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTile = 64;   // transpose tile (elements per side)
+
+inline int row_threads(int chunks) { return chunks >= 1024 ? 1024 : ((chunks + 63) / 64) * 64; }
+
+template <typename T>
+__device__ __forceinline__ float load_f(const T* p, size_t i);
+template <>
+__device__ __forceinline__ float load_f<float>(const float* p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_f<bf16_t>(const bf16_t* p, size_t i) { return bf16_to_f32(p[i].bits); }
+
+template <typename T>
+__device__ __forceinline__ T store_f(float v);
+template <>
+__device__ __forceinline__ float store_f<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ bf16_t store_f<bf16_t>(float v) { return bf16_t{f32_to_bf16(v)}; }
+
+// Sum of a per-thread value over the block, in a fixed order (wave butterflies, then the
+// waves in order); the result is valid in thread 0.  `red` holds one float per wave.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    v = wave_sum_f32(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float s = 0.0f;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+    __syncthreads();
+    return s;
+}
+
+// ---- combine backward: one workgroup per token, one thread per 16-byte chunk ----
+// dy[p] = w[t][j] * dout[t] (rounded once) and dw[t][j] = <dout[t], y[p]> (fp32, chunk order
+// per thread, then the fixed block reduction).  Slots go 8 at a time.
+template <typename T>
+__global__ __launch_bounds__(1024) void combine_bwd_kernel(const uint4* __restrict__ dout,
+                                                           const uint4* __restrict__ y,
+                                                           const int32_t* __restrict__ dest_pos,
+                                                           const float* __restrict__ tw,
+                                                           uint4* __restrict__ dy,
+                                                           float* __restrict__ dw, int k,
+                                                           int N, int chunks) {
+    constexpr int P = 16 / sizeof(T) == 8 ? 8 : 4;
+    __shared__ float red[16][8];
+    const int t = blockIdx.x;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        float part[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) part[g] = 0.0f;
+        for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+            float d[P];
+            unpack16(dout[(size_t)t * chunks + c], d, T{});
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                const int j = j0 + g;
+                if (j >= k) break;
+                const int p = dest_pos[(size_t)t * k + j];
+                if (p < 0 || p >= N) continue;          // an invalid routing entry
+                float v[P], o[P];
+                unpack16(y[(size_t)p * chunks + c], v, T{});
+                const float w = tw[(size_t)t * k + j];
+#pragma unroll
+                for (int i = 0; i < P; ++i) {
+                    part[g] = fmaf(d[i], v[i], part[g]);
+                    o[i] = w * d[i];
+                }
+                dy[(size_t)p * chunks + c] = pack16(o, T{});
+            }
+        }
+        const int wv = threadIdx.x >> 6;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const float s = wave_sum_f32(part[g]);
+            if ((threadIdx.x & 63) == 0) red[wv][g] = s;
+        }
+        __syncthreads();
+        if (threadIdx.x < 8 && j0 + (int)threadIdx.x < k) {
+            float s = 0.0f;
+            for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i][threadIdx.x];
+            dw[(size_t)t * k + j0 + threadIdx.x] = s;
+        }
+        __syncthreads();
+    }
+}
+
+// ---- token gradient: dx[t] = sum_j dxd[dest_pos[t][j]] + sum_j dl[t][j] * Wg[e_tj] ----
+template <typename T>
+__global__ __launch_bounds__(1024) void token_grad_kernel(const uint4* __restrict__ dxd,
+                                                          const int32_t* __restrict__ dest_pos,
+                                                          const float* __restrict__ dl,
+                                                          const int32_t* __restrict__ te,
+                                                          const uint4* __restrict__ wg,
+                                                          uint4* __restrict__ dx, int k,
+                                                          int N, int chunks) {
+    constexpr int P = 16 / sizeof(T) == 8 ? 8 : 4;
+    const int t = blockIdx.x;
+    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+        float acc[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) acc[i] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int p = dest_pos[(size_t)t * k + j];
+            if (p < 0 || p >= N) continue;              // an invalid routing entry
+            float v[P];
+            unpack16(dxd[(size_t)p * chunks + c], v, T{});
+#pragma unroll
+            for (int i = 0; i < P; ++i) acc[i] += v[i];
+        }
+        for (int j = 0; j < k; ++j) {
+            float v[P];
+            unpack16(wg[(size_t)te[(size_t)t * k + j] * chunks + c], v, T{});
+            const float d = dl[(size_t)t * k + j];
+#pragma unroll
+            for (int i = 0; i < P; ++i) acc[i] = fmaf(d, v[i], acc[i]);
+        }
+        dx[(size_t)t * chunks + c] = pack16(acc, T{});
+    }
+}
+
+// ---- gate: logit gradients of the picks, one wave per token ----
+// Picked logits are recomputed (x[t] . Wg[e] + bias, fp32), lane j < k holds pick j.
+template <typename T>
+__global__ __launch_bounds__(256) void gate_dl_kernel(const T* __restrict__ x,
+                                                      const T* __restrict__ wg,
+                                                      const float* __restrict__ bias,
+                                                      const int32_t* __restrict__ te,
+                                                      const float* __restrict__ dw, int routing,
+                                                      int T_, int H, int k, float* __restrict__ dl) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T_) return;                            // whole wave
+    float mine = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        const int e = te[(size_t)t * k + j];
+        float s = 0.0f;
+        for (int h = lane; h < H; h += 64)
+            s = fmaf(load_f(x, (size_t)t * H + h), load_f(wg, (size_t)e * H + h), s);
+        s = wave_sum_f32(s);
+        if (bias) s += bias[e];
+        if (lane == j) mine = s;
+    }
+    const bool act = lane < k;
+    float w, sg = 0.0f, S = 0.0f;
+    if (routing == 0) {
+        float m = act ? mine : -INFINITY;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        const float ex = act ? __expf(mine - m) : 0.0f;
+        w = ex / wave_sum_f32(ex);
+    } else {
+        sg = act ? 1.0f / (1.0f + __expf(-mine)) : 0.0f;
+        S = wave_sum_f32(sg);
+        w = sg / S;
+    }
+    const float dwj = act ? dw[(size_t)t * k + lane] : 0.0f;
+    const float wdw = wave_sum_f32(act ? w * dwj : 0.0f);
+    if (act) {
+        const float r = dwj - wdw;
+        dl[(size_t)t * k + lane] = routing == 0 ? w * r : r / S * sg * (1.0f - sg);
+    }
+}
+
+// DL^T [E][ld]: dl at (e_tj, t), zero elsewhere and in the padding columns t >= T.
+template <typename T>
+__global__ __launch_bounds__(256) void gate_dlt_kernel(const float* __restrict__ dl,
+                                                       const int32_t* __restrict__ te, int T_,
+                                                       int E, int k, int ld, T* __restrict__ dlt) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long long)E * ld) return;
+    const int e = (int)(i / ld), t = (int)(i - (long long)e * ld);
+    float v = 0.0f;
+    if (t < T_)
+        for (int j = 0; j < k; ++j)
+            if (te[(size_t)t * k + j] == e) v = dl[(size_t)t * k + j];
+    dlt[i] = store_f<T>(v);
+}
+
+// dbias[e] = sum of dl over expert e's buffer rows (ascending row order per thread, then the
+// fixed block reduction); one workgroup per expert.
+__global__ __launch_bounds__(256) void gate_dbias_kernel(const float* __restrict__ dl,
+                                                         const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ token_ids,
+                                                         const int32_t* __restrict__ dest_pos,
+                                                         int k, float* __restrict__ dbias) {
+    __shared__ float red[4];
+    const int e = blockIdx.x;
+    float s = 0.0f;
+    for (int p = offsets[e] + threadIdx.x; p < offsets[e + 1]; p += 256) {
+        const int t = token_ids[p];
+        for (int j = 0; j < k; ++j)
+            if (dest_pos[(size_t)t * k + j] == p) s += dl[(size_t)t * k + j];
+    }
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) dbias[e] = s;
+}
+
+// ---- SwiGLU backward, elementwise: dag[p] = (da[0..F), dg[0..F)) ----
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ dh,
+                                                         const T* __restrict__ a,
+                                                         const T* __restrict__ g, long long n,
+                                                         int F, T* __restrict__ dag) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const long long p = i / F;
+    const int f = (int)(i - p * F);
+    const float av = load_f(a, i), gv = load_f(g, i), d = load_f(dh, i);
+    const float sg = 1.0f / (1.0f + __expf(-av));
+    dag[p * 2 * F + f] = store_f<T>(d * gv * sg * (1.0f + av * (1.0f - sg)));
+    dag[p * 2 * F + F + f] = store_f<T>(d * av * sg);
+}
+
+// ---- transposes (64 x 64 tiles through LDS) ----
+// Per expert e (grid z): out[e][c][col0 + r] = in[e][r][c] for r < R, c < C; experts with
+// counts[e] == 0 are skipped when counts is not NULL.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, T* __restrict__ out,
+                                                        int R, int C, long long in_es,
+                                                        long long out_es, int out_ld, int col0,
+                                                        const int32_t* __restrict__ counts) {
+    __shared__ T tile[kTile][kTile + 1];
+    const int e = blockIdx.z;
+    if (counts && counts[e] == 0) return;
+    const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const T* src = in + (size_t)e * in_es;
+    for (int r = ty; r < kTile; r += 4)
+        if (r0 + r < R && c0 + tx < C) tile[r][tx] = src[(size_t)(r0 + r) * C + c0 + tx];
+    __syncthreads();
+    T* dst = out + (size_t)e * out_es;
+    for (int c = ty; c < kTile; c += 4)
+        if (c0 + c < C && r0 + tx < R) dst[(size_t)(c0 + c) * out_ld + col0 + r0 + tx] = tile[tx][c];
+}
+
+// Segment transpose: out[c][q] = in[src(q)][c] for q < Kmax, with src(q) = row pmap[q]
+// (through gather when not NULL) or zero where pmap[q] < 0; pmap NULL: q itself for q < R.
+template <typename T>
+__global__ __launch_bounds__(256) void seg_transpose_kernel(const T* __restrict__ in, int C,
+                                                            const int32_t* __restrict__ gather,
+                                                            const int32_t* __restrict__ pmap,
+                                                            int R, int kmax, T* __restrict__ out) {
+    __shared__ T tile[kTile][kTile + 1];
+    const int q0 = blockIdx.x * kTile, c0 = blockIdx.y * kTile;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int r = ty; r < kTile; r += 4) {
+        const int q = q0 + r;
+        int p = -1;
+        if (q < kmax) p = pmap ? pmap[q] : (q < R ? q : -1);
+        if (p >= 0 && gather) p = gather[p];
+        tile[r][tx] = (p >= 0 && c0 + tx < C) ? in[(size_t)p * C + c0 + tx] : store_f<T>(0.0f);
+    }
+    __syncthreads();
+    for (int c = ty; c < kTile; c += 4)
+        if (c0 + c < C && q0 + tx < kmax) out[(size_t)(c0 + c) * kmax + q0 + tx] = tile[tx][c];
+}
+
+// kofs[e] = sum_{e' < e} round_up(counts[e'], 64); one workgroup of 1024 threads (E <= 1024).
+__global__ __launch_bounds__(1024) void kofs_kernel(const int32_t* __restrict__ counts, int E,
+                                                    int32_t* __restrict__ kofs) {
+    __shared__ int scan[2][1024];
+    const int e = threadIdx.x;
+    const int v = e < E ? (counts[e] + kTile - 1) / kTile * kTile : 0;
+    int cur = 0;
+    scan[0][e] = v;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int s = scan[cur][e] + (e >= d ? scan[cur][e - d] : 0);
+        scan[cur ^ 1][e] = s;
+        cur ^= 1;
+        __syncthreads();
+    }
+    if (e < E) kofs[e] = scan[cur][e] - v;
+    if (e == E - 1) kofs[E] = scan[cur][e];
+}
+
+// pmap[q] = buffer row of column q (-1 in padding): block e < E covers expert e's block,
+// block E the tail [kofs[E], kmax).
+__global__ __launch_bounds__(256) void pmap_kernel(const int32_t* __restrict__ offsets,
+                                                   const int32_t* __restrict__ kofs, int E,
+                                                   int kmax, int32_t* __restrict__ pmap) {
+    const int e = blockIdx.x;
+    const int q0 = kofs[e], q1 = e < E ? kofs[e + 1] : kmax;
+    const int n = e < E ? offsets[e + 1] - offsets[e] : 0, base = e < E ? offsets[e] : 0;
+    for (int q = q0 + threadIdx.x; q < q1; q += 256) pmap[q] = q - q0 < n ? base + (q - q0) : -1;
+}
+
+template <typename T>
+hipError_t transpose_experts(const void* in, void* out, int E, int R, int C, long long in_es,
+                             long long out_es, int out_ld, int col0, const int32_t* counts,
+                             hipStream_t s) {
+    const dim3 grid((C + kTile - 1) / kTile, (R + kTile - 1) / kTile, E);
+    hipLaunchKernelGGL(transpose_kernel<T>, grid, dim3(256), 0, s, static_cast<const T*>(in),
+                       static_cast<T*>(out), R, C, in_es, out_es, out_ld, col0, counts);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t seg_transpose(const void* in, int C, const int32_t* gather, const int32_t* pmap, int R,
+                         int kmax, void* out, hipStream_t s) {
+    const dim3 grid((kmax + kTile - 1) / kTile, (C + kTile - 1) / kTile);
+    hipLaunchKernelGGL(seg_transpose_kernel<T>, grid, dim3(256), 0, s, static_cast<const T*>(in),
+                       C, gather, pmap, R, kmax, static_cast<T*>(out));
+    return hipGetLastError();
+}
+
+size_t align_up(size_t v) { return (v + 255) / 256 * 256; }
+
+// Workspace layout of the layer backward (every piece 256-byte aligned).
+struct BwdWs {
+    void *gemm, *w2t, *w13t, *dy, *dh, *a, *g, *dag, *dxd, *dyt, *ht, *xdt, *dagt, *dlt, *xt;
+    float *dw, *dl;
+    int32_t *kofs, *pmap, *gofs;
+    int kmax, tpad;
+    size_t bytes;
+};
+
+BwdWs carve_bwd(void* base, int dt, int T, int H, int E, int F, int k) {
+    const size_t es = dt == 0 ? 4 : 2;
+    const long long N = (long long)T * k;
+    BwdWs w{};
+    w.kmax = (int)((N + kTile - 1) / kTile * kTile + (long long)kTile * E);
+    w.tpad = (T + kTile - 1) / kTile * kTile;
+    char* p = static_cast<char*>(base);
+    size_t off = 0;
+    auto take = [&](size_t n) -> void* {
+        void* r = p ? p + off : nullptr;
+        off += align_up(n);
+        return r;
+    };
+    w.gemm = take(gemm_ws_bytes(N, E));
+    w.w2t = take(es * E * F * H);
+    w.w13t = take(es * E * H * 2 * F);
+    w.dy = take(es * N * H);
+    w.dh = take(es * N * F);
+    w.a = take(es * N * F);
+    w.g = take(es * N * F);
+    w.dag = take(es * N * 2 * F);
+    w.dxd = take(es * N * H);
+    w.dyt = take(es * H * w.kmax);
+    w.ht = take(es * F * w.kmax);
+    w.xdt = take(es * H * w.kmax);
+    w.dagt = take(es * 2 * F * w.kmax);
+    w.dlt = take(es * E * w.tpad);
+    w.xt = take(es * H * w.tpad);
+    w.dw = static_cast<float*>(take(4 * N));
+    w.dl = static_cast<float*>(take(4 * N));
+    w.kofs = static_cast<int32_t*>(take(4 * (E + 1)));
+    w.pmap = static_cast<int32_t*>(take(4 * (size_t)w.kmax));
+    w.gofs = static_cast<int32_t*>(take(8));
+    w.bytes = off;
+    return w;
+}
+
+__global__ void set_gofs_kernel(int32_t* gofs, int tpad) {
+    if (threadIdx.x == 0) {
+        gofs[0] = 0;
+        gofs[1] = tpad;
+    }
+}
+
+template <typename T>
+hipError_t layer_backward_t(const BwdParams& b, hipStream_t s) {
+    const int T_ = b.T, H = b.H, E = b.E, F = b.F, k = b.k, dt = b.dt;
+    const int N = T_ * k;
+    const BwdWs w = carve_bwd(b.ws, dt, T_, H, E, F, k);
+    const int chunks_h = (int)((size_t)H * sizeof(T) / 16);
+    hipError_t err;
+#define MOE_CHECK(expr)                            \
+    do {                                           \
+        err = (expr);                              \
+        if (err != hipSuccess) return err;         \
+    } while (0)
+    // combine backward: dy, dw (into the caller's dtw when given)
+    float* dw = b.dtw ? b.dtw : w.dw;
+    hipLaunchKernelGGL(combine_bwd_kernel<T>, dim3(T_), dim3(row_threads(chunks_h)), 0, s,
+                       static_cast<const uint4*>(b.dout), static_cast<const uint4*>(b.y), b.dest_pos,
+                       b.top_weights, static_cast<uint4*>(w.dy), dw, k, N, chunks_h);
+    MOE_CHECK(hipGetLastError());
+    // transposed weights of the active experts: W2t [E][F][H], W13t [E][H][2F]
+    MOE_CHECK(transpose_experts<T>(b.w2, w.w2t, E, H, F, (long long)H * F, (long long)F * H, H, 0,
+                                   b.counts, s));
+    MOE_CHECK(transpose_experts<T>(b.w1, w.w13t, E, F, H, (long long)F * H, (long long)H * 2 * F,
+                                   2 * F, 0, b.counts, s));
+    MOE_CHECK(transpose_experts<T>(b.w3, w.w13t, E, F, H, (long long)F * H, (long long)H * 2 * F,
+                                   2 * F, F, b.counts, s));
+    // dh = dy . W2[e];  a, g recomputed;  dag = SwiGLU backward;  dxd = dag . [W1; W3]
+    MOE_CHECK(launch_grouped_nt(dt, N, E, H, F, w.dy, b.offsets, w.w2t, (long long)F * H, w.dh,
+                                w.gemm, s));
+    const void* act = b.xd ? b.xd : b.x;
+    const int32_t* gather = b.xd ? nullptr : b.token_ids;
+    MOE_CHECK(launch_grouped_pair(dt, N, E, H, F, act, gather, T_, b.offsets, b.w1, b.w3, w.a, w.g,
+                                  w.gemm, s));
+    const long long nf = (long long)N * F;
+    hipLaunchKernelGGL(swiglu_bwd_kernel<T>, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const T*>(w.dh), static_cast<const T*>(w.a),
+                       static_cast<const T*>(w.g), nf, F, static_cast<T*>(w.dag));
+    MOE_CHECK(hipGetLastError());
+    MOE_CHECK(launch_grouped_nt(dt, N, E, 2 * F, H, w.dag, b.offsets, w.w13t,
+                                (long long)H * 2 * F, w.dxd, w.gemm, s));
+    // per-expert column blocks for the weight gradients
+    hipLaunchKernelGGL(kofs_kernel, dim3(1), dim3(1024), 0, s, b.counts, E, w.kofs);
+    MOE_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(pmap_kernel, dim3(E + 1), dim3(256), 0, s, b.offsets, w.kofs, E, w.kmax, w.pmap);
+    MOE_CHECK(hipGetLastError());
+    MOE_CHECK(seg_transpose<T>(w.dy, H, nullptr, w.pmap, N, w.kmax, w.dyt, s));
+    MOE_CHECK(seg_transpose<T>(b.h, F, nullptr, w.pmap, N, w.kmax, w.ht, s));
+    MOE_CHECK(seg_transpose<T>(act, H, gather, w.pmap, N, w.kmax, w.xdt, s));
+    MOE_CHECK(seg_transpose<T>(w.dag, 2 * F, nullptr, w.pmap, N, w.kmax, w.dagt, s));
+    const size_t es = sizeof(T);
+    MOE_CHECK(launch_wgrad(dt, E, H, F, w.kmax, w.dyt, w.ht, w.kofs, b.dw2, s));
+    MOE_CHECK(launch_wgrad(dt, E, F, H, w.kmax, w.dagt, w.xdt, w.kofs, b.dw1, s));
+    MOE_CHECK(launch_wgrad(dt, E, F, H, w.kmax, static_cast<const char*>(w.dagt) + es * F * w.kmax,
+                           w.xdt, w.kofs, b.dw3, s));
+    // gate: dl, then dx (dispatch backward + gate), dWg and dbias
+    hipLaunchKernelGGL(gate_dl_kernel<T>, dim3((T_ + 3) / 4), dim3(256), 0, s,
+                       static_cast<const T*>(b.x), static_cast<const T*>(b.wg), b.bias, b.top_experts,
+                       dw, b.routing, T_, H, k, w.dl);
+    MOE_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(token_grad_kernel<T>, dim3(T_), dim3(row_threads(chunks_h)), 0, s,
+                       static_cast<const uint4*>(w.dxd), b.dest_pos, w.dl, b.top_experts,
+                       static_cast<const uint4*>(b.wg), static_cast<uint4*>(b.dx), k, N, chunks_h);
+    MOE_CHECK(hipGetLastError());
+    const long long nd = (long long)E * w.tpad;
+    hipLaunchKernelGGL(gate_dlt_kernel<T>, dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, s, w.dl,
+                       b.top_experts, T_, E, k, w.tpad, static_cast<T*>(w.dlt));
+    MOE_CHECK(hipGetLastError());
+    MOE_CHECK(seg_transpose<T>(b.x, H, nullptr, nullptr, T_, w.tpad, w.xt, s));
+    hipLaunchKernelGGL(set_gofs_kernel, dim3(1), dim3(64), 0, s, w.gofs, w.tpad);
+    MOE_CHECK(hipGetLastError());
+    MOE_CHECK(launch_wgrad(dt, 1, E, H, w.tpad, w.dlt, w.xt, w.gofs, b.dwg, s));
+    hipLaunchKernelGGL(gate_dbias_kernel, dim3(E), dim3(256), 0, s, w.dl, b.offsets, b.token_ids,
+                       b.dest_pos, k, b.dbias);
+    MOE_CHECK(hipGetLastError());
+#undef MOE_CHECK
+    return hipSuccess;
+}
+
+}  // namespace
+
+size_t backward_ws_bytes(int dt, int T, int H, int E, int F, int k) {
+    return carve_bwd(nullptr, dt, T, H, E, F, k).bytes;
+}
+
+hipError_t launch_layer_backward(const BwdParams& b, hipStream_t s) {
+    if (b.T == 0) return hipSuccess;
+    return b.dt == 0 ? layer_backward_t<float>(b, s) : layer_backward_t<bf16_t>(b, s);
+}
+
+}  // namespace moe

@@ -28,7 +28,8 @@ namespace {
 
 constexpr int kThreads = 512;   // 4 compute waves + 4 loader waves
 
-enum Epilogue { kEpiLogits = 0, kEpiSwiGLU = 1, kEpiStore = 2 };
+// kEpiPair (NB = 2) stores both products, a to out and g to out2 (the backward needs them).
+enum Epilogue { kEpiLogits = 0, kEpiSwiGLU = 1, kEpiStore = 2, kEpiPair = 3 };
 
 // Tile shapes.  Expert products: 128 tokens; up product 128 features x 2 operands, down
 // product 256 features; a 3-slot ring of 48 KiB k-slices (64 k per row, whole 128-byte
@@ -80,6 +81,7 @@ struct GemmParams {
     const int* table_count; // [0] entries in table, [1] entries in stable
     int dense_rows;         // rows of the single expert of a dense product (gate)
     void* out;              // [rows][n_feat]: fp32 partial logits or storage type
+    void* out2;             // kEpiPair: the second operand's product
     int k_slices;           // dense product: k-slices per K split
 };
 
@@ -383,40 +385,46 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
         return;
     }
     char* stg = lds + wave * (BT / 2) * kPitch;
+    const int tok0 = row0 + wt * (BT / 2), feat0 = f0 + wf * (BF / 2);
+    constexpr int kOuts = EPI == kEpiPair ? 2 : 1;
 #pragma unroll
-    for (int i = 0; i < FT; ++i) {
+    for (int ob = 0; ob < kOuts; ++ob) {
+        // (one wave's LDS operations run in order, so the second pass's writes come after
+        // the first pass's reads of the same region)
 #pragma unroll
-        for (int j = 0; j < TT; ++j) {
+        for (int i = 0; i < FT; ++i) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float r[4];
+            for (int j = 0; j < TT; ++j) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float a = acc[0][i][j][4 * g + v];
-                    if constexpr (EPI == kEpiSwiGLU) r[v] = silu(a) * acc[NB - 1][i][j][4 * g + v];
-                    else r[v] = a;
-                }
-                char* dst = stg + (j * 32 + l32) * kPitch + (i * 32 + 8 * g + 4 * lhalf) * (int)sizeof(OutT);
-                if constexpr (sizeof(OutT) == 4) {
-                    *reinterpret_cast<float4*>(dst) = make_float4(r[0], r[1], r[2], r[3]);
-                } else {
-                    *reinterpret_cast<uint2*>(dst) =
-                        make_uint2(f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16),
-                                   f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16));
+                for (int g = 0; g < 4; ++g) {
+                    float r[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float a = acc[ob][i][j][4 * g + v];
+                        if constexpr (EPI == kEpiSwiGLU) r[v] = silu(a) * acc[NB - 1][i][j][4 * g + v];
+                        else r[v] = a;
+                    }
+                    char* dst = stg + (j * 32 + l32) * kPitch + (i * 32 + 8 * g + 4 * lhalf) * (int)sizeof(OutT);
+                    if constexpr (sizeof(OutT) == 4) {
+                        *reinterpret_cast<float4*>(dst) = make_float4(r[0], r[1], r[2], r[3]);
+                    } else {
+                        *reinterpret_cast<uint2*>(dst) =
+                            make_uint2(f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16),
+                                       f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16));
+                    }
                 }
             }
         }
-    }
-    const int tok0 = row0 + wt * (BT / 2), feat0 = f0 + wf * (BF / 2);
-    OutT* out = static_cast<OutT*>(p.out);
+        OutT* out = static_cast<OutT*>(ob == 0 ? p.out : p.out2);
 #pragma unroll
-    for (int k = 0; k < kOutChunks / 64; ++k) {
-        const int c = lane + 64 * k;
-        const int r = c / kCpr, cc = c - r * kCpr;
-        const int tok = tok0 + r, feat = feat0 + cc * (16 / (int)sizeof(OutT));
-        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kPitch + cc * 16);
-        if (tok < row_end && feat < p.n_feat)            // n_feat is a multiple of 4 here
-            *reinterpret_cast<uint4*>(out + (size_t)tok * p.n_feat + feat) = v;
+        for (int k = 0; k < kOutChunks / 64; ++k) {
+            const int c = lane + 64 * k;
+            const int r = c / kCpr, cc = c - r * kCpr;
+            const int tok = tok0 + r, feat = feat0 + cc * (16 / (int)sizeof(OutT));
+            const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kPitch + cc * 16);
+            if (tok < row_end && feat < p.n_feat)            // n_feat is a multiple of 4 here
+                *reinterpret_cast<uint4*>(out + (size_t)tok * p.n_feat + feat) = v;
+        }
     }
 }
 
@@ -671,6 +679,133 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
         dn, tl.cap * dn.feat_tiles, max_small * dn.feat_tiles, s);
 }
 
+// ---- backward products ----
+// Generic grouped NT product over the expert segments: out[p][f] = sum_k act[p][k] *
+// w[e][f][k] for rows p of expert e, with the forward's tile table and the 128 x 256 tile.
+template <typename T>
+hipError_t grouped_nt_t(int N, int E, int K, int n_feat, const void* act,
+                        const int32_t* offsets, const void* w, long long w_stride, void* out,
+                        void* ws, hipStream_t s) {
+    constexpr int BT = kExpertBTok, BF = kExpertDownBF, STAGES = kExpertStages,
+                  RB = kExpertRowBytes;
+    const TableLayout tl = carve_tables(ws, N, E);
+    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, N, BT, kSmallBTok,
+                       tl.cap, tl.table, tl.stable, tl.count);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int max_small = kSmallBTok > 0 ? (E < N ? E : N) : 0;
+    GemmParams<T, 1> q{};
+    q.act = static_cast<const T*>(act);
+    q.act_rows = N;
+    q.K = K;
+    q.w[0] = static_cast<const T*>(w);
+    q.w_stride = w_stride;
+    q.n_feat = n_feat;
+    q.feat_tiles = (n_feat + BF - 1) / BF;
+    q.table = tl.table;
+    q.stable = tl.stable;
+    q.table_count = tl.count;
+    q.out = out;
+    return launch_expert<T, 1, kEpiStore, BT, BF, STAGES, RB>(q, tl.cap * q.feat_tiles,
+                                                              max_small * q.feat_tiles, s);
+}
+
+// The up product with both results stored: a = act.W1[e]^T, g = act.W3[e]^T (rows gathered
+// through `gather` when it is not NULL, as in the forward).
+template <typename T>
+hipError_t grouped_pair_t(int N, int E, int H, int F, const void* act, const int32_t* gather,
+                          int src_rows, const int32_t* offsets, const void* w1, const void* w3,
+                          void* a, void* g, void* ws, hipStream_t s) {
+    constexpr int BT = kExpertBTok, BF = kExpertUpBF, STAGES = kExpertStages,
+                  RB = kExpertRowBytes;
+    const TableLayout tl = carve_tables(ws, N, E);
+    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, N, BT, kSmallBTok,
+                       tl.cap, tl.table, tl.stable, tl.count);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int max_small = kSmallBTok > 0 ? (E < N ? E : N) : 0;
+    GemmParams<T, 2> q{};
+    q.act = static_cast<const T*>(act);
+    q.act_rows = N;
+    q.gather = gather;
+    q.src_rows = src_rows;
+    q.K = H;
+    q.w[0] = static_cast<const T*>(w1);
+    q.w[1] = static_cast<const T*>(w3);
+    q.w_stride = (long long)F * H;
+    q.n_feat = F;
+    q.feat_tiles = (F + BF - 1) / BF;
+    q.table = tl.table;
+    q.stable = tl.stable;
+    q.table_count = tl.count;
+    q.out = a;
+    q.out2 = g;
+    return launch_expert<T, 2, kEpiPair, BT, BF, STAGES, RB>(q, tl.cap * q.feat_tiles,
+                                                             max_small * q.feat_tiles, s);
+}
+
+// Weight gradients: out[e][m][f] = sum over k in [kofs[e], kofs[e+1]) of act[m][k] * w[f][k].
+// act [M][Ktot] and w [n_feat][Ktot] hold every expert's rows as a column block starting at
+// kofs[e] (a multiple of 64, zero padded to a multiple of 64).  Work item (expert, m tile,
+// f tile), XCD-contiguous; an expert with no rows gets a zero gradient.
+template <typename T, int BT, int BF, int S, int RB>
+__global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(GemmParams<T, 1> p,
+                                                            const int32_t* kofs, int E, int M) {
+    __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, 1, S, RB>::kLdsBytes];
+    const int mtiles = (M + BT - 1) / BT;
+    const long long per = (long long)mtiles * p.feat_tiles, total = per * E;
+    const long long chunk = (total + 7) >> 3;
+    const int xcd = blockIdx.x & 7;
+    const long long local = blockIdx.x >> 3;
+    if (local >= chunk) return;
+    const long long L = xcd * chunk + local;
+    if (L >= total) return;
+    const int e = (int)(L / per), rem = (int)(L - e * per);
+    const int mt = rem / p.feat_tiles, ft = rem - mt * p.feat_tiles;
+    GemmParams<T, 1> q = p;
+    q.out = static_cast<T*>(p.out) + (size_t)e * M * p.n_feat;
+    const int k0 = kofs[e], k1 = kofs[e + 1];
+    const int nk = (int)((size_t)(k1 - k0) * sizeof(T) / RB);
+    const int row0 = mt * BT;
+    if (nk <= 0) {                                  // whole workgroup: no barrier is pending
+        constexpr int kPer = 16 / (int)sizeof(T);
+        uint4* o = static_cast<uint4*>(q.out);
+        const int fcs = BF / kPer, fc0 = ft * BF / kPer, fcn = p.n_feat / kPer;
+        for (int i = threadIdx.x; i < BT * fcs; i += kThreads) {
+            const int r = row0 + i / fcs, fc = fc0 + i % fcs;
+            if (r < M && fc < fcn) o[(size_t)r * fcn + fc] = make_uint4(0, 0, 0, 0);
+        }
+        return;
+    }
+    const int s0 = (int)((size_t)k0 * sizeof(T) / RB);
+    if (row0 + BT <= M)
+        compute_tile<T, 1, kEpiStore, BT, BF, S, RB, true>(q, lds, 0, row0, M, ft * BF, s0, nk);
+    else
+        compute_tile<T, 1, kEpiStore, BT, BF, S, RB, false>(q, lds, 0, row0, M, ft * BF, s0, nk);
+}
+
+template <typename T>
+hipError_t wgrad_t(int E, int M, int n_feat, int ktot, const void* act, const void* w,
+                   const int32_t* kofs, void* out, hipStream_t s) {
+    constexpr int BT = kExpertBTok, BF = kExpertDownBF, STAGES = kExpertStages,
+                  RB = kExpertRowBytes;
+    GemmParams<T, 1> q{};
+    q.act = static_cast<const T*>(act);
+    q.act_rows = M;
+    q.K = ktot;
+    q.w[0] = static_cast<const T*>(w);
+    q.w_stride = 0;
+    q.n_feat = n_feat;
+    q.feat_tiles = (n_feat + BF - 1) / BF;
+    q.out = out;
+    const long long items = (long long)E * ((M + BT - 1) / BT) * q.feat_tiles;
+    const long long grid = (items + 7) & ~7LL;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((wgrad_kernel<T, BT, BF, STAGES, RB>), dim3((unsigned)grid), dim3(kThreads),
+                       0, s, q, kofs, E, M);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t gemm_ws_bytes(long long N, int E) {
@@ -705,6 +840,29 @@ hipError_t launch_grouped_gemm_gather(int dt, int N, int E, int H, int F, const 
     if (N == 0) return hipSuccess;
     return dt == 0 ? grouped_t<float>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, ws, s)
                    : grouped_t<bf16_t>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, ws, s);
+}
+
+hipError_t launch_grouped_nt(int dt, int N, int E, int K, int n_feat, const void* act,
+                             const int32_t* offsets, const void* w, long long w_stride,
+                             void* out, void* ws, hipStream_t s) {
+    if (N == 0) return hipSuccess;
+    return dt == 0 ? grouped_nt_t<float>(N, E, K, n_feat, act, offsets, w, w_stride, out, ws, s)
+                   : grouped_nt_t<bf16_t>(N, E, K, n_feat, act, offsets, w, w_stride, out, ws, s);
+}
+
+hipError_t launch_grouped_pair(int dt, int N, int E, int H, int F, const void* act,
+                               const int32_t* gather, int src_rows, const int32_t* offsets,
+                               const void* w1, const void* w3, void* a, void* g, void* ws,
+                               hipStream_t s) {
+    if (N == 0) return hipSuccess;
+    return dt == 0 ? grouped_pair_t<float>(N, E, H, F, act, gather, src_rows, offsets, w1, w3, a, g, ws, s)
+                   : grouped_pair_t<bf16_t>(N, E, H, F, act, gather, src_rows, offsets, w1, w3, a, g, ws, s);
+}
+
+hipError_t launch_wgrad(int dt, int E, int M, int n_feat, int ktot, const void* act,
+                        const void* w, const int32_t* kofs, void* out, hipStream_t s) {
+    return dt == 0 ? wgrad_t<float>(E, M, n_feat, ktot, act, w, kofs, out, s)
+                   : wgrad_t<bf16_t>(E, M, n_feat, ktot, act, w, kofs, out, s);
 }
 
 }  // namespace moe

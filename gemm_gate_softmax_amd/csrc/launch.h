@@ -40,4 +40,39 @@ hipError_t launch_grouped_gemm_gather(int dt, int N, int E, int H, int F, const 
                                       const void* w1, const void* w3, const void* w2, void* h,
                                       void* y, void* ws, hipStream_t s);
 
+// ---- backward ----
+// out[p][f] = sum_k act[p][k] * w[e][f][k] over the expert segments (w advances w_stride
+// elements per expert); ws as for launch_grouped_gemm.
+hipError_t launch_grouped_nt(int dt, int N, int E, int K, int n_feat, const void* act,
+                             const int32_t* offsets, const void* w, long long w_stride,
+                             void* out, void* ws, hipStream_t s);
+// a = act.W1[e]^T and g = act.W3[e]^T, [N][F] each (act rows through gather when not NULL).
+hipError_t launch_grouped_pair(int dt, int N, int E, int H, int F, const void* act,
+                               const int32_t* gather, int src_rows, const int32_t* offsets,
+                               const void* w1, const void* w3, void* a, void* g, void* ws,
+                               hipStream_t s);
+// out[e][m][f] = sum_{k in [kofs[e], kofs[e+1])} act[m][k] * w[f][k]; act [M][ktot],
+// w [n_feat][ktot], kofs multiples of 64.
+hipError_t launch_wgrad(int dt, int E, int M, int n_feat, int ktot, const void* act,
+                        const void* w, const int32_t* kofs, void* out, hipStream_t s);
+
+// The whole layer backward (backward.hip): forward intermediates in, gradients out.
+struct BwdParams {
+    int dt, T, H, E, F, k, routing;
+    const void *x, *wg;
+    const float* bias;
+    const void *w1, *w3, *w2;
+    const int32_t* top_experts;
+    const float* top_weights;
+    const int32_t *counts, *offsets, *token_ids, *dest_pos;
+    const void *xd, *h, *y, *dout;      // xd may be NULL (rows gathered from x)
+    void *dx, *dwg;
+    float* dbias;
+    void *dw1, *dw3, *dw2;
+    float* dtw;                         // may be NULL
+    void* ws;
+};
+size_t backward_ws_bytes(int dt, int T, int H, int E, int F, int k);
+hipError_t launch_layer_backward(const BwdParams& b, hipStream_t s);
+
 }  // namespace moe

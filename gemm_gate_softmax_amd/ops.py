@@ -18,13 +18,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
-MOE_WS_GATE, MOE_WS_PFT, MOE_WS_GEMM, MOE_WS_LAYER = 0, 1, 2, 3
+MOE_WS_GATE, MOE_WS_PFT, MOE_WS_GEMM, MOE_WS_LAYER, MOE_WS_BACKWARD = 0, 1, 2, 3, 4
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_VALUE", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_MISALIGNED", 4: "MOE_ERR_WORKSPACE_TOO_SMALL", 5: "MOE_ERR_LAUNCH"}
 
 ROUTING = {"softmax": 0, "sigmoid": 1}   # moe_routing_t
 EXPORTS = ("moe_workspace_bytes", "moe_status_string", "moe_gate_topk", "moe_pft_build",
-           "moe_dispatch", "moe_grouped_gemm_swiglu", "moe_combine", "moe_layer_forward")
+           "moe_dispatch", "moe_grouped_gemm_swiglu", "moe_combine", "moe_layer_forward",
+           "moe_layer_backward")
 
 
 class MoeError(RuntimeError):
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_gemm_swiglu.argtypes = [i32] * 5 + [vp] * 8 + [sz, vp]
         L.moe_combine.argtypes = [i32] * 4 + [vp] * 5
         L.moe_layer_forward.argtypes = ([i32] * 7 + [vp] * 7 + [ctypes.POINTER(LayerBufs), vp, sz, vp])
+        L.moe_layer_backward.argtypes = ([i32] * 7 + [vp] * 6 + [ctypes.POINTER(LayerBufs)] +
+                                         [vp] * 9 + [sz, vp])
         for f in EXPORTS[2:]:
             getattr(L, f).restype = i32
         _lib = L
@@ -263,3 +266,34 @@ def moe_layer_forward(x, wg, bias, w1, w3, w2, k, out=None, bufs=None, ws=None, 
         _ptr(w2), _ptr(out),
         ctypes.byref(cb), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out, bufs, ws
+
+
+def moe_layer_backward(x, wg, bias, w1, w3, w2, k, bufs, dout, grads=None, ws=None, stream=None,
+                       routing="softmax"):
+    """Layer backward.  bufs: the intermediates of the forward (as returned by
+    moe_layer_forward).  Returns (grads dict: dx, dwg, dbias, dw1, dw3, dw2, dtw; ws)."""
+    dt = dtype_code(x.dtype)
+    T, H = x.shape
+    E, F = w1.shape[0], w1.shape[1]
+    _need(x, "x"), _need(wg, "wg", x.dtype, (E, H)), _need(dout, "dout", x.dtype, (T, H))
+    _need(w1, "w1", x.dtype, (E, F, H)), _need(w3, "w3", x.dtype, (E, F, H))
+    _need(w2, "w2", x.dtype, (E, H, F))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,))
+    if grads is None:
+        dev = x.device
+        grads = dict(dx=torch.empty((T, H), dtype=x.dtype, device=dev),
+                     dwg=torch.empty((E, H), dtype=x.dtype, device=dev),
+                     dbias=torch.empty((E,), dtype=torch.float32, device=dev),
+                     dw1=torch.empty((E, F, H), dtype=x.dtype, device=dev),
+                     dw3=torch.empty((E, F, H), dtype=x.dtype, device=dev),
+                     dw2=torch.empty((E, H, F), dtype=x.dtype, device=dev),
+                     dtw=torch.empty((T, k), dtype=torch.float32, device=dev))
+    ws = workspace(MOE_WS_BACKWARD, T, H, E, F, k, dt, x.device) if ws is None else ws
+    cb = LayerBufs(*[_ptr(bufs[n]) for n, _ in LayerBufs._fields_])
+    _check("moe_layer_backward", lib().moe_layer_backward(
+        dt, T, H, E, F, k, ROUTING[routing], _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3),
+        _ptr(w2), ctypes.byref(cb), _ptr(dout), _ptr(grads["dx"]), _ptr(grads["dwg"]),
+        _ptr(grads["dbias"]), _ptr(grads["dw1"]), _ptr(grads["dw3"]), _ptr(grads["dw2"]),
+        _ptr(grads.get("dtw")), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return grads, ws

@@ -68,7 +68,8 @@ typedef enum {
     MOE_WS_GATE = 0,
     MOE_WS_PFT = 1,
     MOE_WS_GEMM = 2,
-    MOE_WS_LAYER = 3
+    MOE_WS_LAYER = 3,
+    MOE_WS_BACKWARD = 4
 } moe_workspace_kind_t;
 
 /* Bytes of workspace a call needs for these sizes (0 for unsupported arguments, including
@@ -185,6 +186,39 @@ moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k
                                const void *w2, void *out,
                                const moe_layer_bufs *bufs, void *ws, size_t ws_bytes,
                                void *stream);
+
+/*
+ * The layer backward.  The pages present the layer as part of a training system (X-MoE
+ * review, section 三, 训练流程: the forward pass is followed by the backward pass and the
+ * weight update) but give no backward formulas; these are the derivatives of the forward
+ * above for a loss L with dL/dout = dout, the expert picks held fixed:
+ *   dy[p]      = top_weights[t][j] * dout[t],   dtop_weights[t][j] = <dout[t], y[p]>
+ *   dh         = dy . W2[e],   da = dh * g * silu'(a),   dg = dh * silu(a)
+ *                (a, g recomputed from the routed rows; silu'(a) = s (1 + a (1 - s)))
+ *   dxd        = da . W1[e] + dg . W3[e]
+ *   dW2[e]     = sum_p dy[p]^T h[p],  dW1[e] = sum_p da[p]^T xd[p],  dW3[e] = sum_p dg[p]^T xd[p]
+ *   dl (picked logits) from dtop_weights through the routing weights: softmax over the picks,
+ *                dl_j = w_j (dw_j - sum_i w_i dw_i); sigmoid, dl_j = (dw_j - sum_i w_i dw_i) / S
+ *                * s_j (1 - s_j) with s = sigmoid(logit), S = sum of the picks' s
+ *   dx[t]      = sum_j dxd[dest_pos[t][j]] + sum_j dl_tj Wg[e_tj]
+ *   dWg[e]     = sum_t dl_te x[t],   dbias[e] = sum_t dl_te
+ * (p = dest_pos[t][j], e = top_experts[t][j], h and y as the forward stored them).
+ * Inputs: the forward's inputs and its intermediates in *fwd (top_experts, top_weights,
+ * counts, offsets, token_ids, dest_pos, h and y required; xd may be NULL, the rows are
+ * then gathered from x), and dout [T][H].  Outputs: dx [T][H], dwg [E][H], dw1 and dw3
+ * [E][F][H], dw2 [E][H][F] in the storage type; dbias [E] fp32; dtop_weights [T][k] fp32
+ * (may be NULL).  Experts without rows get zero weight gradients.  All accumulation is
+ * fp32, each output is rounded once; results are deterministic (no atomics).
+ * ws: moe_workspace_bytes(MOE_WS_BACKWARD, ...) bytes (transposed weights of every expert,
+ * E*3*F*H elements, plus row-sized intermediates).  T == 0 is a no-op (nothing is written).
+ */
+moe_status_t moe_layer_backward(moe_dtype_t dt, int T, int H, int E, int F, int k,
+                                moe_routing_t routing, const void *x, const void *wg,
+                                const float *bias, const void *w1, const void *w3,
+                                const void *w2, const moe_layer_bufs *fwd, const void *dout,
+                                void *dx, void *dwg, float *dbias, void *dw1, void *dw3,
+                                void *dw2, float *dtop_weights, void *ws, size_t ws_bytes,
+                                void *stream);
 
 #ifdef __cplusplus
 }

@@ -138,3 +138,34 @@ def test_gemm_and_layer_reject(L):
     nb7 = ops.LayerBufs(*([A] * 6 + [None, None, A, A]))  # dest_pos stays required
     assert lf(*args(bufs=nb7)) == INVALID
     assert lf(*args(T=0)) == OK
+
+
+def test_layer_backward_rejects(L):
+    lb = L.moe_layer_backward
+    bufs = ops.LayerBufs(*([A] * 10))
+    args = lambda **kw: [kw.get("dt", 1), kw.get("T", 8), kw.get("H", 64), kw.get("E", 4),
+                         kw.get("F", 64), kw.get("k", 2), kw.get("routing", 0), A, A, None, A,
+                         A, A, ctypes.byref(kw.get("bufs", bufs)), kw.get("dout", A),
+                         A, A, kw.get("dbias", A), A, A, A, kw.get("dtw", None), A,
+                         kw.get("ws", 1 << 40), None]
+    assert lb(*args(k=5)) == UNSUPPORTED
+    assert lb(*args(routing=3)) == INVALID
+    assert lb(*args(F=96 + 1)) == UNSUPPORTED
+    assert lb(*args(ws=100)) == WS_SMALL
+    assert lb(*args(dout=None)) == INVALID
+    assert lb(*args(dbias=MIS)) == MISALIGNED
+    assert lb(*args(dtw=MIS)) == MISALIGNED
+    nh = ops.LayerBufs(*([A] * 8 + [None, A]))          # h is required by the backward
+    assert lb(*args(bufs=nh)) == INVALID
+    xb = ops.LayerBufs(*([A] * 7 + [MIS, A, A]))        # xd may be NULL, never misaligned
+    assert lb(*args(bufs=xb)) == MISALIGNED
+    assert lb(*args(T=0)) == OK
+
+
+def test_backward_workspace_size(L):
+    ws = L.moe_workspace_bytes
+    small = ws(4, 8, 64, 4, 64, 2, 1)
+    assert small > 0 and small % 256 == 0
+    # at least the transposed weights of every expert: E * 3 * F * H elements
+    assert ws(4, 4096, 7168, 256, 2048, 8, 1) >= 256 * 3 * 2048 * 7168 * 2
+    assert ws(4, 8, 64, 4, 100, 2, 1) == 0              # F not a multiple of 64
