@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing moe_layer_backward (reported beside the forward)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain device copies of 1 GiB (counter calibration)")
     ap.add_argument("--up-kernel-only", action="store_true",
@@ -292,6 +294,29 @@ def main():
         "combine_GBs": alg["combine_bytes"] / (st_ms["combine"] * 1e-3) / 1e9,
         "grouped_gemm_GBs": alg["gemm_bytes"] / (g_ms * 1e-3) / 1e9,
     }
+    bwd = None
+    if not args.no_backward:
+        # The layer backward after the fused forward (bufs_f): gradients of x, Wg, bias, W1,
+        # W3 and W2 for a synthetic dout.  Its products: dh, the recomputed a and g, dxd and
+        # three weight gradients, 16 N H F flops against the forward's 6 N H F.
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed + 1)
+        dout = torch.randn((cfg.T, cfg.H), generator=gen, device=dev).to(d["x"].dtype)
+        step()
+        grads, bws = ops.moe_layer_backward(d["x"], d["wg"], d["bias"], d["w1"], d["w3"],
+                                            d["w2"], cfg.k, bufs_f, dout)
+        torch.cuda.synchronize()
+        bsteps = max(1, min(args.steps, 5))
+        bwd_ms = time_calls(lambda: ops.moe_layer_backward(
+            d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k, bufs_f, dout,
+            grads=grads, ws=bws), bsteps, stream)
+        bflops = 16.0 * cfg.N * cfg.H * cfg.F
+        bwd = {"ms_per_step": round(bwd_ms, 3), "tokens_per_s": round(cfg.T / (bwd_ms * 1e-3), 1),
+               "steps": bsteps, "tflops": round(bflops / (bwd_ms * 1e-3) / 1e12, 2),
+               "workspace_GB": round(bws.numel() / 1e9, 2),
+               "note": "moe_layer_backward after the fused forward: dx, dWg, dbias, dW1, dW3, dW2"}
+        del grads, bws, dout
+        torch.cuda.empty_cache()
     if args.verbose:
         for n, v in st_ms.items():
             log(f"  {n:13s} {v * 1e3:9.1f} us")
@@ -333,6 +358,8 @@ def main():
            "grouped_gemm_frac_hbm": round(bw["grouped_gemm_GBs"] / HBM_PEAK_GBS, 4)},
         "wall_ms_per_step": wall_ms,
     }
+    if bwd is not None:
+        rec["backward"] = bwd
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(cfg, d, args.seed, args.cpu_seconds)

@@ -236,48 +236,85 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ d
     dag[p * 2 * F + F + f] = store_f<T>(d * av * sg);
 }
 
-// ---- transposes (64 x 64 tiles through LDS) ----
-// Per expert e (grid z): out[e][c][col0 + r] = in[e][r][c] for r < R, c < C; experts with
-// counts[e] == 0 are skipped when counts is not NULL.
+// ---- transposes (64 x 64 tiles through LDS, 16-byte global accesses) ----
+// Every transposed dimension here is a multiple of 64, so tiles are whole.  A thread reads
+// 16-byte chunks of source rows into LDS (one 32-bit word per element, rows padded by one
+// word), then gathers 16 bytes of a destination row from consecutive source rows.
+template <typename T>
+struct TileIO {
+    static constexpr int kPer = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+    static constexpr int kChunks = kTile * kTile / kPer;
+    __device__ static void put(uint32_t (*tile)[kTile + 1], int r, int c, const uint4& v) {
+        float f[kPer];
+        unpack16(v, f, T{});
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            tile[r][c + i] = sizeof(T) == 4 ? __float_as_uint(f[i]) : (__float_as_uint(f[i]) >> 16);
+    }
+    __device__ static uint4 get(uint32_t (*tile)[kTile + 1], int r, int c) {  // column c, rows r..
+        float f[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            f[i] = sizeof(T) == 4 ? __uint_as_float(tile[r + i][c]) : __uint_as_float(tile[r + i][c] << 16);
+        return pack16(f, T{});
+    }
+};
+
+// Per expert e (grid z): out[e][c][col0 + r] = in[e][r][c] for r < R, c < C (both multiples
+// of 64); experts with counts[e] == 0 are skipped when counts is not NULL.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, T* __restrict__ out,
                                                         int R, int C, long long in_es,
                                                         long long out_es, int out_ld, int col0,
                                                         const int32_t* __restrict__ counts) {
-    __shared__ T tile[kTile][kTile + 1];
+    using IO = TileIO<T>;
+    constexpr int kPer = IO::kPer, kCpr = kTile / kPer;
+    __shared__ uint32_t tile[kTile][kTile + 1];
     const int e = blockIdx.z;
     if (counts && counts[e] == 0) return;
     const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     const T* src = in + (size_t)e * in_es;
-    for (int r = ty; r < kTile; r += 4)
-        if (r0 + r < R && c0 + tx < C) tile[r][tx] = src[(size_t)(r0 + r) * C + c0 + tx];
+    for (int i = threadIdx.x; i < IO::kChunks; i += 256) {
+        const int r = i / kCpr, cc = i - r * kCpr;
+        IO::put(tile, r, cc * kPer,
+                *reinterpret_cast<const uint4*>(src + (size_t)(r0 + r) * C + c0 + cc * kPer));
+    }
     __syncthreads();
     T* dst = out + (size_t)e * out_es;
-    for (int c = ty; c < kTile; c += 4)
-        if (c0 + c < C && r0 + tx < R) dst[(size_t)(c0 + c) * out_ld + col0 + r0 + tx] = tile[tx][c];
+    for (int i = threadIdx.x; i < IO::kChunks; i += 256) {
+        const int c = i / kCpr, rr = i - c * kCpr;
+        *reinterpret_cast<uint4*>(dst + (size_t)(c0 + c) * out_ld + col0 + r0 + rr * kPer) =
+            IO::get(tile, rr * kPer, c);
+    }
 }
 
-// Segment transpose: out[c][q] = in[src(q)][c] for q < Kmax, with src(q) = row pmap[q]
+// Segment transpose: out[c][q] = in[src(q)][c] for q < kmax, with src(q) = row pmap[q]
 // (through gather when not NULL) or zero where pmap[q] < 0; pmap NULL: q itself for q < R.
+// C and kmax are multiples of 64.
 template <typename T>
 __global__ __launch_bounds__(256) void seg_transpose_kernel(const T* __restrict__ in, int C,
                                                             const int32_t* __restrict__ gather,
                                                             const int32_t* __restrict__ pmap,
                                                             int R, int kmax, T* __restrict__ out) {
-    __shared__ T tile[kTile][kTile + 1];
+    using IO = TileIO<T>;
+    constexpr int kPer = IO::kPer, kCpr = kTile / kPer;
+    __shared__ uint32_t tile[kTile][kTile + 1];
     const int q0 = blockIdx.x * kTile, c0 = blockIdx.y * kTile;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int r = ty; r < kTile; r += 4) {
+    for (int i = threadIdx.x; i < IO::kChunks; i += 256) {
+        const int r = i / kCpr, cc = i - r * kCpr;
         const int q = q0 + r;
-        int p = -1;
-        if (q < kmax) p = pmap ? pmap[q] : (q < R ? q : -1);
+        int p = pmap ? pmap[q] : (q < R ? q : -1);
         if (p >= 0 && gather) p = gather[p];
-        tile[r][tx] = (p >= 0 && c0 + tx < C) ? in[(size_t)p * C + c0 + tx] : store_f<T>(0.0f);
+        const uint4 v = p >= 0 ? *reinterpret_cast<const uint4*>(in + (size_t)p * C + c0 + cc * kPer)
+                               : make_uint4(0, 0, 0, 0);
+        IO::put(tile, r, cc * kPer, v);
     }
     __syncthreads();
-    for (int c = ty; c < kTile; c += 4)
-        if (c0 + c < C && q0 + tx < kmax) out[(size_t)(c0 + c) * kmax + q0 + tx] = tile[tx][c];
+    for (int i = threadIdx.x; i < IO::kChunks; i += 256) {
+        const int c = i / kCpr, rr = i - c * kCpr;
+        *reinterpret_cast<uint4*>(out + (size_t)(c0 + c) * kmax + q0 + rr * kPer) =
+            IO::get(tile, rr * kPer, c);
+    }
 }
 
 // kofs[e] = sum_{e' < e} round_up(counts[e'], 64); one workgroup of 1024 threads (E <= 1024).

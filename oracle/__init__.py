@@ -52,7 +52,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_combine.argtypes = [i32] * 4 + [vp] * 4
         L.oracle_layer_forward.argtypes = [i32] * 7 + [vp] * 8
         L.oracle_combine_backward.argtypes = [i32] * 4 + [vp] * 6
-        L.oracle_expert_backward.argtypes = [i32] * 5 + [vp] * 12
+        L.oracle_expert_backward.argtypes = [i32] * 5 + [vp] * 11
         L.oracle_dispatch_backward.argtypes = [i32] * 3 + [vp] * 3
         L.oracle_gate_backward.argtypes = [i32] * 6 + [vp] * 9
         L.oracle_layer_backward.argtypes = [i32] * 7 + [vp] * 14

@@ -111,3 +111,90 @@ def test_experts_without_rows_get_zero_weight_gradients():
     assert len(empty) > 0
     for n in ("dw1", "dw3", "dw2"):
         assert torch.count_nonzero(grads[n][torch.tensor(empty, device=DEV)]).item() == 0, n
+
+
+def _sub_offsets(experts_of_rows):
+    """Compact expert segments for rows already sorted by expert: (unique experts, offsets)."""
+    uniq, counts = np.unique(experts_of_rows, return_counts=True)
+    return uniq, np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("name", ["xmoe_small", "xmoe_large"])
+def test_backward_full_size_sampled(name):
+    """At the benchmark shapes, on the launch the benchmark times: dtw and dx of sampled
+    tokens, all weight gradients of one small expert, dWg and dbias of that expert, and the
+    zero sum of dbias, each against the oracle's stage functions on just the rows involved."""
+    cfg = W.CONFIGS[name]
+    d, dout_h, bufs, grads = _run(cfg, "softmax", fuse=True)
+    dt, k = cfg.dtype, cfg.k
+    te = W.to_host(bufs["top_experts"], None)
+    tw = W.to_host(bufs["top_weights"], None)
+    dp = W.to_host(bufs["dest_pos"], None)
+    off = W.to_host(bufs["offsets"], None)
+    counts = W.to_host(bufs["counts"], None)
+    tok = W.to_host(bufs["token_ids"], None)
+    x_h = W.to_host(d["x"], dt)
+    wg_h = W.to_host(d["wg"], dt)
+    bias_h = W.to_host(d["bias"], None)
+    rng = np.random.default_rng(5)
+
+    def expert_w(e_list):
+        idx = torch.tensor(np.asarray(e_list, np.int64), device=DEV)
+        return [W.to_host(d[n][idx], dt) for n in ("w1", "w3", "w2")]
+
+    def check(got, ref, what, fp32=False):
+        scale = float(np.max(np.abs(ref)))
+        err = float(np.max(np.abs(np.asarray(got, np.float64) - ref)))
+        tol = (FP32_GRAD_TOL if fp32 else BWD_TOL)[dt] * scale
+        print(f"{name} {what}: max err {err:.3e} scale {scale:.3e}", flush=True)
+        assert err <= tol, (what, err, scale)
+
+    # 1. dtw and dx of sampled tokens
+    ts = np.sort(rng.choice(cfg.T, size=4, replace=False))
+    rows = dp[ts].reshape(-1)                                   # their buffer rows
+    y_sub = W.to_host(bufs["y"][torch.tensor(rows.astype(np.int64), device=DEV)], dt)
+    dy_ref, dtw_ref = oracle.combine_backward(dt, dout_h[ts], y_sub,
+                                              np.arange(len(rows), dtype=np.int32).reshape(len(ts), k),
+                                              tw[ts])
+    check(grads["dtw"].cpu().numpy()[ts], dtw_ref, "dtw (sampled tokens)", fp32=True)
+    order = np.argsort(te[ts].reshape(-1), kind="stable")      # group the rows by expert
+    e_rows = te[ts].reshape(-1)[order]
+    uniq, soff = _sub_offsets(e_rows)
+    w1s, w3s, w2s = expert_w(uniq)
+    xd_sub = x_h[np.repeat(ts, k)[order]]
+    h_sub = W.to_host(bufs["h"][torch.tensor(rows[order].astype(np.int64), device=DEV)], dt)
+    eb = oracle.expert_backward(dt, xd_sub, soff, w1s, w3s, w2s, dy_ref[order], h=h_sub)
+    dxd = np.empty_like(eb["dxd"])
+    dxd[order] = eb["dxd"]
+    dx_ref = dxd.reshape(len(ts), k, cfg.H).sum(axis=1)
+    gb = oracle.gate_backward(dt, x_h[ts], wg_h, bias_h, te[ts], dtw_ref, dx=dx_ref)
+    check(as_f64(W.to_host(grads["dx"], dt)[ts], dt), gb["dx"], "dx (sampled tokens)")
+
+    # 2. every weight gradient of one small expert (the fewest rows), from all of its rows
+    active = np.where(counts > 0)[0]
+    e = int(active[np.argmin(counts[active])])
+    prow = np.arange(off[e], off[e + 1])
+    tj = [(int(tok[p]), int(np.where(dp[tok[p]] == p)[0][0])) for p in prow]
+    dy_e = np.stack([tw[t, j] * as_f64(dout_h[t], dt) for t, j in tj])
+    w1s, w3s, w2s = expert_w([e])
+    h_e = W.to_host(bufs["h"][int(off[e]):int(off[e + 1])], dt)
+    eb = oracle.expert_backward(dt, x_h[[t for t, _ in tj]], np.array([0, len(prow)], np.int32),
+                                w1s, w3s, w2s, dy_e, h=h_e)
+    for n in ("dw1", "dw3", "dw2"):
+        check(as_f64(W.to_host(grads[n][e], dt), dt), eb[n][0], f"{n}[{e}] ({len(prow)} rows)")
+
+    # 3. dWg and dbias of that expert, from every token that picked it
+    tpick = np.array(sorted({t for t, _ in tj}))
+    dtw_t = np.zeros((len(tpick), k))
+    for i, t in enumerate(tpick):
+        rows_t = dp[t]
+        yt = W.to_host(bufs["y"][torch.tensor(rows_t.astype(np.int64), device=DEV)], dt)
+        _, dtw_t[i] = oracle.combine_backward(dt, dout_h[[t]], yt,
+                                              np.arange(k, dtype=np.int32).reshape(1, k), tw[[t]])
+    gb = oracle.gate_backward(dt, x_h[tpick], wg_h, bias_h, te[tpick], dtw_t)
+    check(as_f64(W.to_host(grads["dwg"][e], dt), dt), gb["dwg"][e], f"dwg[{e}]")
+    check(grads["dbias"].cpu().numpy()[[e]], gb["dbias"][[e]], f"dbias[{e}]", fp32=True)
+
+    # 4. softmax logit gradients of a token sum to zero, so dbias does too
+    db = grads["dbias"].double().cpu().numpy()
+    assert abs(db.sum()) <= 1e-4 * np.abs(db).sum()

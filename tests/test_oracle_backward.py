@@ -152,3 +152,25 @@ def test_backward_stages_reject_bad_input():
     with pytest.raises(RuntimeError):
         oracle.gate_backward("f32", np.zeros((2, 4), np.float32), np.zeros((3, 4), np.float32),
                              None, np.array([[0], [5]], np.int32), np.zeros((2, 1)))
+
+
+def test_stage_wrappers_compose_to_the_layer_backward():
+    """The per-stage entry points (used by the sampled full-size GPU checks) chained by hand
+    give the whole-layer backward."""
+    cfg = W.LayerConfig("bwd", T=20, H=32, E=6, F=16, k=2, dtype="bf16", bias=("zipf", 1.0))
+    p = W.make_host(cfg, seed=8)
+    dout = W._store(np.random.default_rng(4).standard_normal((cfg.T, cfg.H)), "bf16")
+    te, tw = oracle.gate_topk("bf16", p["x"], p["wg"], p["bias"], cfg.k)
+    b = oracle.pft_build(te, cfg.E)
+    xd = oracle.dispatch("bf16", p["x"], b["dest_pos"])
+    h, y = oracle.grouped_gemm_swiglu("bf16", xd, b["offsets"], p["w1"], p["w3"], p["w2"])
+    dy, dw = oracle.combine_backward("bf16", dout, y, b["dest_pos"], tw)
+    eb = oracle.expert_backward("bf16", xd, b["offsets"], p["w1"], p["w3"], p["w2"], dy, h=h)
+    dx = oracle.dispatch_backward(eb["dxd"], b["dest_pos"])
+    gb = oracle.gate_backward("bf16", p["x"], p["wg"], p["bias"], te, dw, dx=dx)
+    ref = oracle.layer_backward("bf16", p["x"], p["wg"], p["bias"], p["w1"], p["w3"], p["w2"],
+                                cfg.k, dout)
+    assert np.array_equal(gb["dx"], ref["dx"]) and np.array_equal(dw, ref["dtw"])
+    assert np.array_equal(gb["dwg"], ref["dwg"]) and np.array_equal(gb["dbias"], ref["dbias"])
+    for n in ("dw1", "dw3", "dw2"):
+        assert np.array_equal(eb[n], ref[n]), n
