@@ -28,13 +28,6 @@ constexpr int kTile = 64;   // transpose tile (elements per side)
 inline int row_threads(int chunks) { return chunks >= 1024 ? 1024 : ((chunks + 63) / 64) * 64; }
 
 template <typename T>
-__device__ __forceinline__ float load_f(const T* p, size_t i);
-template <>
-__device__ __forceinline__ float load_f<float>(const float* p, size_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float load_f<bf16_t>(const bf16_t* p, size_t i) { return bf16_to_f32(p[i].bits); }
-
-template <typename T>
 __device__ __forceinline__ T store_f(float v);
 template <>
 __device__ __forceinline__ float store_f<float>(float v) { return v; }
@@ -144,14 +137,17 @@ __global__ __launch_bounds__(1024) void token_grad_kernel(const uint4* __restric
 }
 
 // ---- gate: logit gradients of the picks, one wave per token ----
-// Picked logits are recomputed (x[t] . Wg[e] + bias, fp32), lane j < k holds pick j.
+// Picked logits are recomputed (x[t] . Wg[e] + bias, fp32, 16-byte chunks per lane), lane
+// j < k holds pick j.
 template <typename T>
-__global__ __launch_bounds__(256) void gate_dl_kernel(const T* __restrict__ x,
-                                                      const T* __restrict__ wg,
+__global__ __launch_bounds__(256) void gate_dl_kernel(const uint4* __restrict__ x,
+                                                      const uint4* __restrict__ wg,
                                                       const float* __restrict__ bias,
                                                       const int32_t* __restrict__ te,
                                                       const float* __restrict__ dw, int routing,
-                                                      int T_, int H, int k, float* __restrict__ dl) {
+                                                      int T_, int chunks, int k,
+                                                      float* __restrict__ dl) {
+    constexpr int P = 16 / sizeof(T) == 8 ? 8 : 4;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T_) return;                            // whole wave
@@ -159,8 +155,13 @@ __global__ __launch_bounds__(256) void gate_dl_kernel(const T* __restrict__ x,
     for (int j = 0; j < k; ++j) {
         const int e = te[(size_t)t * k + j];
         float s = 0.0f;
-        for (int h = lane; h < H; h += 64)
-            s = fmaf(load_f(x, (size_t)t * H + h), load_f(wg, (size_t)e * H + h), s);
+        for (int c = lane; c < chunks; c += 64) {
+            float a[P], b[P];
+            unpack16(x[(size_t)t * chunks + c], a, T{});
+            unpack16(wg[(size_t)e * chunks + c], b, T{});
+#pragma unroll
+            for (int i = 0; i < P; ++i) s = fmaf(a[i], b[i], s);
+        }
         s = wave_sum_f32(s);
         if (bias) s += bias[e];
         if (lane == j) mine = s;
@@ -220,20 +221,30 @@ __global__ __launch_bounds__(256) void gate_dbias_kernel(const float* __restrict
     if (threadIdx.x == 0) dbias[e] = s;
 }
 
-// ---- SwiGLU backward, elementwise: dag[p] = (da[0..F), dg[0..F)) ----
+// ---- SwiGLU backward, elementwise over 16-byte chunks: dag[p] = (da[0..F), dg[0..F)) ----
 template <typename T>
-__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ dh,
-                                                         const T* __restrict__ a,
-                                                         const T* __restrict__ g, long long n,
-                                                         int F, T* __restrict__ dag) {
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict__ dh,
+                                                         const uint4* __restrict__ a,
+                                                         const uint4* __restrict__ g,
+                                                         long long nchunks, int fchunks,
+                                                         uint4* __restrict__ dag) {
+    constexpr int P = 16 / sizeof(T) == 8 ? 8 : 4;
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    const long long p = i / F;
-    const int f = (int)(i - p * F);
-    const float av = load_f(a, i), gv = load_f(g, i), d = load_f(dh, i);
-    const float sg = 1.0f / (1.0f + __expf(-av));
-    dag[p * 2 * F + f] = store_f<T>(d * gv * sg * (1.0f + av * (1.0f - sg)));
-    dag[p * 2 * F + F + f] = store_f<T>(d * av * sg);
+    if (i >= nchunks) return;
+    const long long p = i / fchunks;
+    const int fc = (int)(i - p * fchunks);
+    float av[P], gv[P], d[P], da[P], dg[P];
+    unpack16(a[i], av, T{});
+    unpack16(g[i], gv, T{});
+    unpack16(dh[i], d, T{});
+#pragma unroll
+    for (int v = 0; v < P; ++v) {
+        const float sg = 1.0f / (1.0f + __expf(-av[v]));
+        da[v] = d[v] * gv[v] * sg * (1.0f + av[v] * (1.0f - sg));
+        dg[v] = d[v] * av[v] * sg;
+    }
+    dag[p * 2 * fchunks + fc] = pack16(da, T{});
+    dag[p * 2 * fchunks + fchunks + fc] = pack16(dg, T{});
 }
 
 // ---- transposes (64 x 64 tiles through LDS, 16-byte global accesses) ----
@@ -317,6 +328,79 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(const T* __restrict_
     }
 }
 
+// ---- weight gradients of small experts: outer products on the vector ALUs ----
+// An expert with at most kOuterRows rows (most of them have one or two) makes a weight
+// gradient that is almost all output: out[e][m][f] = sum_{i < r} a[p_i][aoff + m] *
+// b[src(p_i)][f], p_i = offsets[e] + i, src = gather[p] or p, fp32 FMAs in ascending i, one
+// rounding.  One workgroup per (expert, kOuterM output rows); each thread takes 16-byte
+// chunks of f, so every store instruction writes whole row segments; the rows it reads are
+// the untransposed ones.  Experts without rows get zeros; larger experts are left to the
+// tile GEMM.
+constexpr int kOuterRows = 64;
+constexpr int kOuterM = 16;
+
+template <typename T>
+__global__ __launch_bounds__(256) void wgrad_outer_kernel(const T* __restrict__ a, int lda, int aoff,
+                                                          const T* __restrict__ b, int ldb,
+                                                          const int32_t* __restrict__ gather,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int M, int Nf, T* __restrict__ out) {
+    constexpr int P = 16 / (int)sizeof(T);
+    const int e = blockIdx.y, m0 = blockIdx.x * kOuterM;
+    const int p0 = offsets[e], r = offsets[e + 1] - p0;
+    if (r > kOuterRows) return;                     // whole workgroup
+    T* o = out + ((size_t)e * M + m0) * Nf;
+    const int nfc = Nf / P;
+    for (int fc = threadIdx.x; fc < nfc; fc += 256) {
+        float acc[kOuterM][P];
+#pragma unroll
+        for (int mm = 0; mm < kOuterM; ++mm)
+#pragma unroll
+            for (int v = 0; v < P; ++v) acc[mm][v] = 0.0f;
+        for (int i = 0; i < r; ++i) {
+            const int p = p0 + i;
+            const int src = gather ? gather[p] : p;
+            float bv[P];
+            unpack16(*reinterpret_cast<const uint4*>(b + (size_t)src * ldb + (size_t)fc * P), bv, T{});
+            const uint4* arow = reinterpret_cast<const uint4*>(a + (size_t)p * lda + aoff + m0);
+#pragma unroll
+            for (int q = 0; q < kOuterM / P; ++q) {
+                float av[P];
+                unpack16(arow[q], av, T{});
+#pragma unroll
+                for (int u = 0; u < P; ++u)
+#pragma unroll
+                    for (int v = 0; v < P; ++v) acc[q * P + u][v] = fmaf(av[u], bv[v], acc[q * P + u][v]);
+            }
+        }
+#pragma unroll
+        for (int mm = 0; mm < kOuterM; ++mm)
+            *reinterpret_cast<uint4*>(o + (size_t)mm * Nf + (size_t)fc * P) = pack16(acc[mm], T{});
+    }
+}
+
+// list[0, *nlist) = the experts with more than `small` rows, ascending (one workgroup,
+// E <= 1024).
+__global__ __launch_bounds__(1024) void split_experts_kernel(const int32_t* __restrict__ counts,
+                                                             int E, int small,
+                                                             int32_t* __restrict__ list,
+                                                             int32_t* __restrict__ nlist) {
+    __shared__ int scan[2][1024];
+    const int e = threadIdx.x;
+    const int v = e < E && counts[e] > small ? 1 : 0;
+    int cur = 0;
+    scan[0][e] = v;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int s_ = scan[cur][e] + (e >= d ? scan[cur][e - d] : 0);
+        scan[cur ^ 1][e] = s_;
+        cur ^= 1;
+        __syncthreads();
+    }
+    if (v) list[scan[cur][e] - 1] = e;
+    if (e == 1023) *nlist = scan[cur][e];
+}
+
 // kofs[e] = sum_{e' < e} round_up(counts[e'], 64); one workgroup of 1024 threads (E <= 1024).
 __global__ __launch_bounds__(1024) void kofs_kernel(const int32_t* __restrict__ counts, int E,
                                                     int32_t* __restrict__ kofs) {
@@ -372,7 +456,7 @@ size_t align_up(size_t v) { return (v + 255) / 256 * 256; }
 struct BwdWs {
     void *gemm, *w2t, *w13t, *dy, *dh, *a, *g, *dag, *dxd, *dyt, *ht, *xdt, *dagt, *dlt, *xt;
     float *dw, *dl;
-    int32_t *kofs, *pmap, *gofs;
+    int32_t *kofs, *pmap, *gofs, *elist, *nlist;
     int kmax, tpad;
     size_t bytes;
 };
@@ -410,6 +494,8 @@ BwdWs carve_bwd(void* base, int dt, int T, int H, int E, int F, int k) {
     w.kofs = static_cast<int32_t*>(take(4 * (E + 1)));
     w.pmap = static_cast<int32_t*>(take(4 * (size_t)w.kmax));
     w.gofs = static_cast<int32_t*>(take(8));
+    w.elist = static_cast<int32_t*>(take(4 * (size_t)E));
+    w.nlist = static_cast<int32_t*>(take(4));
     w.bytes = off;
     return w;
 }
@@ -453,10 +539,11 @@ hipError_t layer_backward_t(const BwdParams& b, hipStream_t s) {
     const int32_t* gather = b.xd ? nullptr : b.token_ids;
     MOE_CHECK(launch_grouped_pair(dt, N, E, H, F, act, gather, T_, b.offsets, b.w1, b.w3, w.a, w.g,
                                   w.gemm, s));
-    const long long nf = (long long)N * F;
-    hipLaunchKernelGGL(swiglu_bwd_kernel<T>, dim3((unsigned)((nf + 255) / 256)), dim3(256), 0, s,
-                       static_cast<const T*>(w.dh), static_cast<const T*>(w.a),
-                       static_cast<const T*>(w.g), nf, F, static_cast<T*>(w.dag));
+    const int fchunks = (int)((size_t)F * sizeof(T) / 16);
+    const long long nfc = (long long)N * fchunks;
+    hipLaunchKernelGGL(swiglu_bwd_kernel<T>, dim3((unsigned)((nfc + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint4*>(w.dh), static_cast<const uint4*>(w.a),
+                       static_cast<const uint4*>(w.g), nfc, fchunks, static_cast<uint4*>(w.dag));
     MOE_CHECK(hipGetLastError());
     MOE_CHECK(launch_grouped_nt(dt, N, E, 2 * F, H, w.dag, b.offsets, w.w13t,
                                 (long long)H * 2 * F, w.dxd, w.gemm, s));
@@ -469,15 +556,30 @@ hipError_t layer_backward_t(const BwdParams& b, hipStream_t s) {
     MOE_CHECK(seg_transpose<T>(b.h, F, nullptr, w.pmap, N, w.kmax, w.ht, s));
     MOE_CHECK(seg_transpose<T>(act, H, gather, w.pmap, N, w.kmax, w.xdt, s));
     MOE_CHECK(seg_transpose<T>(w.dag, 2 * F, nullptr, w.pmap, N, w.kmax, w.dagt, s));
+    // weight gradients: experts with at most kOuterRows rows (or none) as outer products,
+    // the others on the tile GEMM over their column blocks
+    hipLaunchKernelGGL(split_experts_kernel, dim3(1), dim3(1024), 0, s, b.counts, E, kOuterRows,
+                       w.elist, w.nlist);
+    MOE_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(wgrad_outer_kernel<T>, dim3(H / kOuterM, E), dim3(256), 0, s,
+                       static_cast<const T*>(w.dy), H, 0, static_cast<const T*>(b.h), F, nullptr,
+                       b.offsets, H, F, static_cast<T*>(b.dw2));
+    MOE_CHECK(hipGetLastError());
+    for (int half = 0; half < 2; ++half) {
+        hipLaunchKernelGGL(wgrad_outer_kernel<T>, dim3(F / kOuterM, E), dim3(256), 0, s,
+                           static_cast<const T*>(w.dag), 2 * F, half * F, static_cast<const T*>(act), H,
+                           gather, b.offsets, F, H, static_cast<T*>(half ? b.dw3 : b.dw1));
+        MOE_CHECK(hipGetLastError());
+    }
     const size_t es = sizeof(T);
-    MOE_CHECK(launch_wgrad(dt, E, H, F, w.kmax, w.dyt, w.ht, w.kofs, b.dw2, s));
-    MOE_CHECK(launch_wgrad(dt, E, F, H, w.kmax, w.dagt, w.xdt, w.kofs, b.dw1, s));
+    MOE_CHECK(launch_wgrad(dt, E, H, F, w.kmax, w.dyt, w.ht, w.kofs, w.elist, w.nlist, b.dw2, s));
+    MOE_CHECK(launch_wgrad(dt, E, F, H, w.kmax, w.dagt, w.xdt, w.kofs, w.elist, w.nlist, b.dw1, s));
     MOE_CHECK(launch_wgrad(dt, E, F, H, w.kmax, static_cast<const char*>(w.dagt) + es * F * w.kmax,
-                           w.xdt, w.kofs, b.dw3, s));
+                           w.xdt, w.kofs, w.elist, w.nlist, b.dw3, s));
     // gate: dl, then dx (dispatch backward + gate), dWg and dbias
     hipLaunchKernelGGL(gate_dl_kernel<T>, dim3((T_ + 3) / 4), dim3(256), 0, s,
-                       static_cast<const T*>(b.x), static_cast<const T*>(b.wg), b.bias, b.top_experts,
-                       dw, b.routing, T_, H, k, w.dl);
+                       static_cast<const uint4*>(b.x), static_cast<const uint4*>(b.wg), b.bias,
+                       b.top_experts, dw, b.routing, T_, chunks_h, k, w.dl);
     MOE_CHECK(hipGetLastError());
     hipLaunchKernelGGL(token_grad_kernel<T>, dim3(T_), dim3(row_threads(chunks_h)), 0, s,
                        static_cast<const uint4*>(w.dxd), b.dest_pos, w.dl, b.top_experts,
@@ -490,7 +592,7 @@ hipError_t layer_backward_t(const BwdParams& b, hipStream_t s) {
     MOE_CHECK(seg_transpose<T>(b.x, H, nullptr, nullptr, T_, w.tpad, w.xt, s));
     hipLaunchKernelGGL(set_gofs_kernel, dim3(1), dim3(64), 0, s, w.gofs, w.tpad);
     MOE_CHECK(hipGetLastError());
-    MOE_CHECK(launch_wgrad(dt, 1, E, H, w.tpad, w.dlt, w.xt, w.gofs, b.dwg, s));
+    MOE_CHECK(launch_wgrad(dt, 1, E, H, w.tpad, w.dlt, w.xt, w.gofs, nullptr, nullptr, b.dwg, s));
     hipLaunchKernelGGL(gate_dbias_kernel, dim3(E), dim3(256), 0, s, w.dl, b.offsets, b.token_ids,
                        b.dest_pos, k, b.dbias);
     MOE_CHECK(hipGetLastError());

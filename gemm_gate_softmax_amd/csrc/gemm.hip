@@ -250,10 +250,17 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
                 if (i_ >= kActDma && WNT) dma16_nt(src[i_] + o_, b_ + i_ * 4096);           \
                 else if (i_ >= kActDma || i_ < nact) dma16(src[i_] + o_, b_ + i_ * 4096);     \
         } while (0)
-        for (int s = 0; s < S - 1; ++s) MOE_ISSUE(min(s, nk - 1), s);
-        // barrier 0: stage 0 landed
-        if constexpr (FULL) wait_vm_and_barrier<(S - 2) * kDma, false>();
-        else wait_vm_and_barrier_rt<(S - 2) * (kDma - kActDma), (S - 2) * kDma>((S - 2) * keff);
+        if (nk == 1) {
+            // a single k-slice (weight gradients of experts with at most 64 rows): no
+            // clamped copies, nothing follows barrier 0
+            MOE_ISSUE(0, 0);
+            wait_vm_and_barrier<0, false>();
+        } else {
+            for (int s = 0; s < S - 1; ++s) MOE_ISSUE(min(s, nk - 1), s);
+            // barrier 0: stage 0 landed
+            if constexpr (FULL) wait_vm_and_barrier<(S - 2) * kDma, false>();
+            else wait_vm_and_barrier_rt<(S - 2) * (kDma - kActDma), (S - 2) * kDma>((S - 2) * keff);
+        }
         int refill = S - 1;
         for (int kt = 0; kt < nk - 1; ++kt) {
             MOE_ISSUE(min(kt + S - 1, nk - 1), refill);             // slot of stage kt-1
@@ -747,20 +754,25 @@ hipError_t grouped_pair_t(int N, int E, int H, int F, const void* act, const int
 // Weight gradients: out[e][m][f] = sum over k in [kofs[e], kofs[e+1]) of act[m][k] * w[f][k].
 // act [M][Ktot] and w [n_feat][Ktot] hold every expert's rows as a column block starting at
 // kofs[e] (a multiple of 64, zero padded to a multiple of 64).  Work item (expert, m tile,
-// f tile), XCD-contiguous; an expert with no rows gets a zero gradient.
+// f tile), XCD-contiguous, over every expert or over the experts listed in elist[0, *nlist);
+// an expert with no rows gets a zero gradient.
 template <typename T, int BT, int BF, int S, int RB>
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(GemmParams<T, 1> p,
-                                                            const int32_t* kofs, int E, int M) {
+                                                            const int32_t* kofs, int E, int M,
+                                                            const int32_t* elist,
+                                                            const int32_t* nlist) {
     __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, 1, S, RB>::kLdsBytes];
     const int mtiles = (M + BT - 1) / BT;
-    const long long per = (long long)mtiles * p.feat_tiles, total = per * E;
+    // XCD chunks over the items that exist (the grid is sized for E experts)
+    const long long per = (long long)mtiles * p.feat_tiles, total = per * (elist ? *nlist : E);
     const long long chunk = (total + 7) >> 3;
     const int xcd = blockIdx.x & 7;
     const long long local = blockIdx.x >> 3;
     if (local >= chunk) return;
     const long long L = xcd * chunk + local;
     if (L >= total) return;
-    const int e = (int)(L / per), rem = (int)(L - e * per);
+    const int i = (int)(L / per), rem = (int)(L - (long long)i * per);
+    const int e = elist ? elist[i] : i;             // with a list, its i-th expert
     const int mt = rem / p.feat_tiles, ft = rem - mt * p.feat_tiles;
     GemmParams<T, 1> q = p;
     q.out = static_cast<T*>(p.out) + (size_t)e * M * p.n_feat;
@@ -786,7 +798,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(GemmParams<T, 1> p,
 
 template <typename T>
 hipError_t wgrad_t(int E, int M, int n_feat, int ktot, const void* act, const void* w,
-                   const int32_t* kofs, void* out, hipStream_t s) {
+                   const int32_t* kofs, const int32_t* elist, const int32_t* nlist, void* out,
+                   hipStream_t s) {
     constexpr int BT = kExpertBTok, BF = kExpertDownBF, STAGES = kExpertStages,
                   RB = kExpertRowBytes;
     GemmParams<T, 1> q{};
@@ -802,7 +815,7 @@ hipError_t wgrad_t(int E, int M, int n_feat, int ktot, const void* act, const vo
     const long long grid = (items + 7) & ~7LL;
     if (grid <= 0) return hipSuccess;
     hipLaunchKernelGGL((wgrad_kernel<T, BT, BF, STAGES, RB>), dim3((unsigned)grid), dim3(kThreads),
-                       0, s, q, kofs, E, M);
+                       0, s, q, kofs, E, M, elist, nlist);
     return hipGetLastError();
 }
 
@@ -860,9 +873,10 @@ hipError_t launch_grouped_pair(int dt, int N, int E, int H, int F, const void* a
 }
 
 hipError_t launch_wgrad(int dt, int E, int M, int n_feat, int ktot, const void* act,
-                        const void* w, const int32_t* kofs, void* out, hipStream_t s) {
-    return dt == 0 ? wgrad_t<float>(E, M, n_feat, ktot, act, w, kofs, out, s)
-                   : wgrad_t<bf16_t>(E, M, n_feat, ktot, act, w, kofs, out, s);
+                        const void* w, const int32_t* kofs, const int32_t* elist,
+                        const int32_t* nlist, void* out, hipStream_t s) {
+    return dt == 0 ? wgrad_t<float>(E, M, n_feat, ktot, act, w, kofs, elist, nlist, out, s)
+                   : wgrad_t<bf16_t>(E, M, n_feat, ktot, act, w, kofs, elist, nlist, out, s);
 }
 
 }  // namespace moe

@@ -52,9 +52,11 @@ hipError_t launch_grouped_pair(int dt, int N, int E, int H, int F, const void* a
                                const void* w1, const void* w3, void* a, void* g, void* ws,
                                hipStream_t s);
 // out[e][m][f] = sum_{k in [kofs[e], kofs[e+1])} act[m][k] * w[f][k]; act [M][ktot],
-// w [n_feat][ktot], kofs multiples of 64.
+// w [n_feat][ktot], kofs multiples of 64.  With elist (device, may be NULL) only the experts
+// elist[0, *nlist) are computed, E being an upper bound of *nlist.
 hipError_t launch_wgrad(int dt, int E, int M, int n_feat, int ktot, const void* act,
-                        const void* w, const int32_t* kofs, void* out, hipStream_t s);
+                        const void* w, const int32_t* kofs, const int32_t* elist,
+                        const int32_t* nlist, void* out, hipStream_t s);
 
 // The whole layer backward (backward.hip): forward intermediates in, gradients out.
 struct BwdParams {
