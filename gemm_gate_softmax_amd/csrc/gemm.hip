@@ -53,6 +53,10 @@ constexpr int kExpertDownBF = MOE_EXPERT_DOWN_BF;
 constexpr int kExpertStages = MOE_EXPERT_STAGES;
 constexpr int kExpertRowBytes = MOE_EXPERT_RB;
 constexpr int kGroupTok = MOE_GROUP_TOK;   // token tiles per L2-sharing block (expert_gemm_kernel)
+#ifndef MOE_INTERLEAVE_READS
+#define MOE_INTERLEAVE_READS 1
+#endif
+constexpr bool kInterleave = MOE_INTERLEAVE_READS != 0;
 // Experts with at most kSmallBTok rows get one small tile: kSmallBTok tokens, the same
 // features, a kSmallStages-slot ring.  Such a tile is mostly a weight stream; in its own
 // list it can be spread evenly among the MFMA-heavy tiles of the large experts, and its
@@ -311,6 +315,20 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
             _Pragma("unroll") for (int i = 0; i < FT; ++i) FW[b][i] = *reinterpret_cast<const uint4*>( \
                 st_ + (BT + b * BF + wf * (BF / 2) + i * 32 + l32) * kRowBytes + cs_);      \
     } while (0)
+    // Scheduling hint: one fragment read after each MFMA, so reads issue while the MFMA
+    // pipe is busy rather than as a block between two MFMA runs.
+    constexpr int kMfmaPerStep = NB * FT * TT, kReadsPerStep = TT + NB * FT;
+#define MOE_INTERLEAVE()                                                                      \
+    do {                                                                                     \
+        if constexpr (kInterleave) {                                                         \
+            _Pragma("unroll") for (int q_ = 0; q_ < kMfmaPerStep; ++q_) {                    \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           \
+                if (q_ < kReadsPerStep) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   \
+            }                                                                                \
+            if constexpr (kReadsPerStep > kMfmaPerStep)                                      \
+                __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerStep - kMfmaPerStep, 0); \
+        }                                                                                    \
+    } while (0)
 #define MOE_MFMAS(FA, FW)                                                                     \
     do {                                                                                     \
         _Pragma("unroll") for (int b = 0; b < NB; ++b)                                       \
@@ -329,18 +347,23 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
 #pragma unroll
         for (int ks = 0; ks < KS; ks += 2) {
             MOE_LOAD_FRAGS(st, ks + 1, fa1, fw1);
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!kInterleave) __builtin_amdgcn_sched_barrier(0);
             MOE_MFMAS(fa0, fw0);
+            MOE_INTERLEAVE();
             __builtin_amdgcn_sched_barrier(0);
             if (ks + 2 < KS) {
                 MOE_LOAD_FRAGS(st, ks + 2, fa0, fw0);
+                if constexpr (!kInterleave) __builtin_amdgcn_sched_barrier(0);
+                MOE_MFMAS(fa1, fw1);
+                MOE_INTERLEAVE();
             } else {
                 __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (3 << 14));   // lgkmcnt(0)
                 __builtin_amdgcn_s_barrier();                        // barrier kt+1
                 MOE_LOAD_FRAGS(lds + next * kStageBytes, 0, fa0, fw0);
+                if constexpr (!kInterleave) __builtin_amdgcn_sched_barrier(0);
+                MOE_MFMAS(fa1, fw1);
+                MOE_INTERLEAVE();
             }
-            __builtin_amdgcn_sched_barrier(0);
-            MOE_MFMAS(fa1, fw1);
             __builtin_amdgcn_sched_barrier(0);
         }
         slot = next;
@@ -357,6 +380,7 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
     }
 #undef MOE_LOAD_FRAGS
 #undef MOE_MFMAS
+#undef MOE_INTERLEAVE
 
     // ---- epilogue: lane holds one token and, per 32-feature tile, 4 runs of 4 features ----
     // Outputs go through LDS: each wave writes its (BT/2) x (BF/2) block into a region of
