@@ -57,6 +57,17 @@ constexpr int kGroupTok = MOE_GROUP_TOK;   // token tiles per L2-sharing block (
 #define MOE_INTERLEAVE_READS 1
 #endif
 constexpr bool kInterleave = MOE_INTERLEAVE_READS != 0;
+// A large tile starts its K loop at slice (j mod P) * nk / P, j its position in its XCD's
+// dispatch order, and wraps around: the ~32 tiles an XCD runs at once, started one after
+// another as CUs free up, then tend to read the same k-slice of their shared operand panels
+// at the same time, so the panels are fetched into L2 once rather than once per tile.  At
+// X-MoE Large, P = 32 cuts L2->fabric reads 25% (19.7 -> 14.7 GB per up launch) and the
+// layer by 1.3%; P = 16 and 64 read more and ran slower.  0 switches it off.
+#ifndef MOE_K_ROTATE
+#define MOE_K_ROTATE 32
+#endif
+constexpr bool kRotate = MOE_K_ROTATE != 0;
+constexpr int kRotPeriod = MOE_K_ROTATE > 0 ? MOE_K_ROTATE : 1;
 // Experts with at most kSmallBTok rows get one small tile: kSmallBTok tokens, the same
 // features, a kSmallStages-slot ring.  Such a tile is mostly a weight stream; in its own
 // list it can be spread evenly among the MFMA-heavy tiles of the large experts, and its
@@ -185,10 +196,12 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
 // barrier per stage hands the slots over: before barrier kt every loader has seen stage kt
 // land and every compute wave has finished reading stage kt-1, so after it stage kt is
 // read while stage kt+S-1 is loaded into the slot stage kt-1 left.  WNT marks the weight
-// transfers non-temporal: for a tile that is the only reader of its weights.
+// transfers non-temporal: for a tile that is the only reader of its weights.  The tile
+// visits k-slices rot, rot+1, ..., nk-1, 0, ..., rot-1 of its K range (rot < nk).
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool FULL, bool WNT = false>
 __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* lds, int expert,
-                                             int row0, int row_end, int f0, int s0, int nk) {
+                                             int row0, int row_end, int f0, int s0, int nk,
+                                             int rot = 0) {
     using Tile = CompTile<BT, BF, NB, S, RB>;
     constexpr int kRowBytes = Tile::kRowBytes;
     constexpr int kRowsPerDma = 1024 / kRowBytes;    // rows per 1 KiB DMA instruction
@@ -249,7 +262,8 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
 #define MOE_ISSUE(KT, SLOT)                                                                   \
         do {                                                                                 \
             const uint32_t b_ = __builtin_amdgcn_readfirstlane(wbase + (SLOT) * kStageBytes); \
-            const size_t o_ = (size_t)(KT) * kRowBytes;                                      \
+            const int ks_ = (KT) + rot;                                                      \
+            const size_t o_ = (size_t)(ks_ >= nk ? ks_ - nk : ks_) * kRowBytes;              \
             _Pragma("unroll") for (int i_ = 0; i_ < kDma; ++i_)                              \
                 if (i_ >= kActDma && WNT) dma16_nt(src[i_] + o_, b_ + i_ * 4096);           \
                 else if (i_ >= kActDma || i_ < nact) dma16(src[i_] + o_, b_ + i_ * 4096);     \
@@ -531,10 +545,11 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, 
         const int ftile = ql / width;
         const int ttile = blk * kGroupTok + (ql - ftile * width);
         const int row0 = seg0 + ttile * BT, row_end = min(seg0 + segn, p.act_rows);
+        const int rot = kRotate ? (j % kRotPeriod) * nk / kRotPeriod : 0;
         if (row_end - row0 >= BT)
-            compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, expert, row0, row_end, ftile * BF, 0, nk);
+            compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot);
         else
-            compute_tile<T, NB, EPI, BT, BF, S, RB, false>(p, lds, expert, row0, row_end, ftile * BF, 0, nk);
+            compute_tile<T, NB, EPI, BT, BF, S, RB, false>(p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot);
     } else if constexpr (kSmallBTok > 0) {
         constexpr int SB = kSmallBTok > 0 ? kSmallBTok : 64;
         const int Ls = xcd * chunk_s + (j - a0);
