@@ -109,8 +109,9 @@ def algorithmic(cfg, counts):
         active_experts=active,
         gemm_flops=6.0 * N * H * F,
         up_flops=4.0 * N * H * F,
-        # the up kernel reads each active expert's W1 and W3 once, xd once, writes h once
-        up_bytes=active * 2.0 * F * H * b + b * (N * H + N * F),
+        # the up kernel with the dispatch fused (as in the timed step) reads each active
+        # expert's W1 and W3 once and the token rows x once, and writes h once
+        up_bytes=active * 2.0 * F * H * b + b * (T * H + N * F),
         gemm_bytes=active * 3.0 * H * F * b + b * (2.0 * N * H + 2.0 * N * F),
         dispatch_bytes=b * (T * H + N * H) + 4.0 * N,
         combine_bytes=b * (N * H + T * H) + 8.0 * N,
@@ -205,9 +206,9 @@ def main():
             d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k, out=out, bufs=bufs, ws=ws)
         step_staged_once()
         gws0 = ops.workspace(ops.MOE_WS_GEMM, cfg.N, cfg.H, cfg.E, cfg.F, 1, dtc, dev)
-        for _ in range(args.steps):
-            ops.moe_grouped_gemm_swiglu(bufs["xd"], bufs["offsets"], d["w1"], d["w3"], None,
-                                        h=bufs["h"], ws=gws0)
+        for _ in range(args.steps):     # the up product as the layer runs it (dispatch fused)
+            ops.moe_grouped_gemm_swiglu(d["x"], bufs["offsets"], d["w1"], d["w3"], None,
+                                        h=bufs["h"], ws=gws0, token_ids=bufs["token_ids"])
         torch.cuda.synchronize()
         print(json.dumps({"up_kernel_only": args.steps, "workload": cfg.name}), flush=True)
         return 0
@@ -257,9 +258,11 @@ def main():
         fn()
         torch.cuda.synchronize()
         st_ms[name] = time_calls(fn, args.steps, stream)
-    # The dominant kernel alone: the gate/up product (tile table + one expert launch).
-    up_call = lambda: ops.moe_grouped_gemm_swiglu(bufs["xd"], bufs["offsets"], d["w1"], d["w3"],
-                                                  None, h=bufs["h"], ws=gws)
+    # The dominant kernel alone, as the timed step runs it: the gate/up product with the
+    # dispatch fused (rows gathered from x through token_ids; tile table + one expert launch).
+    up_call = lambda: ops.moe_grouped_gemm_swiglu(d["x"], bufs_f["offsets"], d["w1"], d["w3"],
+                                                  None, h=bufs_f["h"], ws=gws,
+                                                  token_ids=bufs_f["token_ids"])
     up_call()
     torch.cuda.synchronize()
     up_ms = time_calls(up_call, args.steps, stream)
@@ -337,7 +340,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof | {
             "traffic": recorded_traffic(cfg.name),
-            "kernel": "expert_gemm_kernel, gate/up product + SwiGLU",
+            "kernel": "expert_gemm_kernel, gate/up product + SwiGLU, dispatch fused (as in the timed step)",
             "per_launch": {"flop": alg["up_flops"], "bytes": alg["up_bytes"],
                            "us": round(up_ms * 1e3, 1), "flop_per_byte": round(intensity, 1),
                            "ridge_flop_per_byte": round(ridge, 1),

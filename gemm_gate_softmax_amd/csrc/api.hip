@@ -129,7 +129,8 @@ MOE_API moe_status_t moe_dispatch(moe_dtype_t dt, int T, int k, int H, const voi
 }
 
 MOE_API moe_status_t moe_grouped_gemm_swiglu(moe_dtype_t dt, int N, int E, int H, int F,
-                                             const void* xd, const int32_t* offsets,
+                                             const void* xd, const int32_t* token_ids,
+                                             int src_rows, const int32_t* offsets,
                                              const void* w1, const void* w3, const void* w2,
                                              void* h, void* y, void* ws, size_t ws_bytes,
                                              void* stream) {
@@ -139,10 +140,16 @@ MOE_API moe_status_t moe_grouped_gemm_swiglu(moe_dtype_t dt, int N, int E, int H
     MOE_TRY(check_dim(H));
     MOE_TRY(check_dim(F));
     if ((w2 == nullptr) != (y == nullptr)) return MOE_ERR_INVALID_VALUE;
+    if (token_ids && src_rows < 1) return MOE_ERR_INVALID_VALUE;
     if (N == 0) return MOE_OK;
     MOE_TRY(check_ptrs({xd, offsets, w1, w3, h, ws}));
     if (w2) MOE_TRY(check_ptrs({w2, y}));
+    if (token_ids) MOE_TRY(check_ptrs({token_ids}));
     if (ws_bytes < gemm_ws(N, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (token_ids)
+        return launched(moe::launch_grouped_gemm_gather(dt, N, E, H, F, xd, src_rows, token_ids,
+                                                        offsets, w1, w3, w2, h, y, ws,
+                                                        as_stream(stream)));
     return launched(moe::launch_grouped_gemm(dt, N, E, H, F, xd, offsets, w1, w3, w2, h, y, ws,
                                              as_stream(stream)));
 }

@@ -60,7 +60,7 @@ def lib() -> ctypes.CDLL:
         L.moe_gate_topk.argtypes = [i32] * 6 + [vp] * 6 + [sz, vp]
         L.moe_pft_build.argtypes = [i32] * 3 + [vp] * 7 + [sz, vp]
         L.moe_dispatch.argtypes = [i32] * 4 + [vp] * 4
-        L.moe_grouped_gemm_swiglu.argtypes = [i32] * 5 + [vp] * 8 + [sz, vp]
+        L.moe_grouped_gemm_swiglu.argtypes = [i32] * 5 + [vp] * 2 + [i32] + [vp] * 7 + [sz, vp]
         L.moe_combine.argtypes = [i32] * 4 + [vp] * 5
         L.moe_layer_forward.argtypes = ([i32] * 7 + [vp] * 7 + [ctypes.POINTER(LayerBufs), vp, sz, vp])
         L.moe_layer_backward.argtypes = ([i32] * 7 + [vp] * 6 + [ctypes.POINTER(LayerBufs)] +
@@ -187,13 +187,19 @@ def moe_dispatch(x, dest_pos, xd=None, stream=None):
     return xd
 
 
-def moe_grouped_gemm_swiglu(xd, offsets, w1, w3, w2, h=None, y=None, ws=None, stream=None):
+def moe_grouped_gemm_swiglu(xd, offsets, w1, w3, w2, h=None, y=None, ws=None, stream=None,
+                            token_ids=None):
     """SwiGLU experts over the ragged segments.  Returns (h [N,F], y [N,H]).
 
     w2=None computes only h (the gate/up product and its SwiGLU) and returns (h, None).
+    token_ids given: xd holds the token rows x [T,H] and product row p reads
+    x[token_ids[p]] (the dispatch fused into the up product); N = token_ids.numel().
     """
     dt = dtype_code(xd.dtype)
-    N, H = xd.shape
+    src_rows, H = xd.shape
+    N = src_rows if token_ids is None else token_ids.numel()
+    if token_ids is not None:
+        _need(token_ids, "token_ids", torch.int32, (N,))
     E, F = w1.shape[0], w1.shape[1]
     _need(xd, "xd"), _need(offsets, "offsets", torch.int32, (E + 1,))
     _need(w1, "w1", xd.dtype, (E, F, H)), _need(w3, "w3", xd.dtype, (E, F, H))
@@ -209,8 +215,8 @@ def moe_grouped_gemm_swiglu(xd, offsets, w1, w3, w2, h=None, y=None, ws=None, st
     if ws is None:  # sized for N = T*k rows: pass T = N, k = 1
         ws = workspace(MOE_WS_GEMM, N, H, E, F, 1, dt, xd.device)
     _check("moe_grouped_gemm_swiglu", lib().moe_grouped_gemm_swiglu(
-        dt, N, E, H, F, _ptr(xd), _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(h), _ptr(y),
-        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+        dt, N, E, H, F, _ptr(xd), _ptr(token_ids), src_rows, _ptr(offsets), _ptr(w1), _ptr(w3),
+        _ptr(w2), _ptr(h), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return h, y
 
 

@@ -139,11 +139,17 @@ moe_status_t moe_dispatch(moe_dtype_t dt, int T, int k, int H, const void *x,
  * (holds the device-built tile table; sized from N = T*k and E).
  * w2 and y both NULL: only h is computed (the gate/up product and its SwiGLU); exactly
  * one of them NULL is MOE_ERR_INVALID_VALUE.
+ * token_ids not NULL: the dispatch is fused into the up product.  xd then points at the
+ * token rows x [src_rows][H] and product row p reads x[token_ids[p]] (token_ids [N], as from
+ * moe_pft_build; ids are clamped to [0, src_rows)), which gives the same h and y as
+ * moe_dispatch followed by this call; src_rows < 1 is MOE_ERR_INVALID_VALUE.  token_ids
+ * NULL: xd is [N][H] and src_rows is ignored.
  */
 moe_status_t moe_grouped_gemm_swiglu(moe_dtype_t dt, int N, int E, int H, int F,
-                                     const void *xd, const int32_t *offsets, const void *w1,
-                                     const void *w3, const void *w2, void *h, void *y,
-                                     void *ws, size_t ws_bytes, void *stream);
+                                     const void *xd, const int32_t *token_ids, int src_rows,
+                                     const int32_t *offsets, const void *w1, const void *w3,
+                                     const void *w2, void *h, void *y, void *ws,
+                                     size_t ws_bytes, void *stream);
 
 /*
  * Padding-free weighted combine (X-MoE review, 训练流程 step 6; FlashDMoE blog, section 1.1:

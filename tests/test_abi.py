@@ -109,7 +109,9 @@ def test_move_rejects(L):
 
 
 def test_gemm_and_layer_reject(L):
-    g = L.moe_grouped_gemm_swiglu
+    L_g = L.moe_grouped_gemm_swiglu
+    # (dt, N, E, H, F, xd, offsets, w1, w3, w2, h, y, ws, ws_bytes, stream), token_ids NULL
+    g = lambda dt, N, E, H, F, xd, *rest: L_g(dt, N, E, H, F, xd, None, 0, *rest)
     assert g(1, 100, 8, 64, 100, A, A, A, A, A, A, A, A, 1 << 20, None) == UNSUPPORTED  # F % 64
     assert g(1, 100, 0, 64, 64, A, A, A, A, A, A, A, A, 1 << 20, None) == INVALID      # E < 1
     assert g(1, 100, 8, 64, 64, A, A, A, A, A, A, A, A, 0, None) == WS_SMALL
@@ -119,6 +121,9 @@ def test_gemm_and_layer_reject(L):
     assert g(1, 100, 8, 64, 64, A, A, A, A, None, A, A, A, 1 << 20, None) == INVALID
     assert g(1, 100, 8, 64, 64, A, A, A, A, A, A, None, A, 1 << 20, None) == INVALID
     assert g(1, 100, 8, 64, 64, A, A, A, A, None, None, None, A, 1 << 20, None) == INVALID  # h
+    # fused dispatch: token_ids needs src_rows >= 1 and an aligned pointer
+    assert L_g(1, 100, 8, 64, 64, A, A, 0, A, A, A, A, A, A, A, 1 << 20, None) == INVALID
+    assert L_g(1, 100, 8, 64, 64, A, MIS, 10, A, A, A, A, A, A, A, 1 << 20, None) == MISALIGNED
     lf = L.moe_layer_forward
     bufs = ops.LayerBufs(*([A] * 10))
     args = lambda **kw: [kw.get("dt", 1), kw.get("T", 8), kw.get("H", 64), kw.get("E", 4),
