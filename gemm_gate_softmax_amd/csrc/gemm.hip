@@ -53,16 +53,27 @@ constexpr int kExpertDownBF = MOE_EXPERT_DOWN_BF;
 constexpr int kExpertStages = MOE_EXPERT_STAGES;
 constexpr int kExpertRowBytes = MOE_EXPERT_RB;
 constexpr int kGroupTok = MOE_GROUP_TOK;   // token tiles per L2-sharing block (expert_gemm_kernel)
+// The same when the activation rows are gathered from the token rows (the dispatch fused
+// into the up product): x is T rows, which stay in the caches, so sharing a weight panel
+// among more token tiles pays.  At X-MoE Large the fused layer measured 4.27 / 4.23 / 4.19 /
+// 4.16 ms for blocks of 8 / 12 / 16 / 32, while the product reading xd slows from 2.87 to
+// 3.09 ms at 32.
+#ifndef MOE_GROUP_TOK_GATHER
+#define MOE_GROUP_TOK_GATHER 32
+#endif
+constexpr int kGroupTokGather = MOE_GROUP_TOK_GATHER;
 #ifndef MOE_INTERLEAVE_READS
 #define MOE_INTERLEAVE_READS 1
 #endif
 constexpr bool kInterleave = MOE_INTERLEAVE_READS != 0;
-// A large tile starts its K loop at slice (j mod P) * nk / P, j its position in its XCD's
-// dispatch order, and wraps around: the ~32 tiles an XCD runs at once, started one after
-// another as CUs free up, then tend to read the same k-slice of their shared operand panels
-// at the same time, so the panels are fetched into L2 once rather than once per tile.  At
-// X-MoE Large, P = 32 cuts L2->fabric reads 25% (19.7 -> 14.7 GB per up launch) and the
-// layer by 1.3%; P = 16 and 64 read more and ran slower.  0 switches it off.
+// A large tile starts its K loop at slice ((ttile + 7 ftile) mod P) * nk / P and wraps
+// around (ttile, ftile: its token and feature tile within the expert).  Tiles that share an
+// operand panel and run at the same time then sit at different points of K, and as CUs free
+// up at different times their slices line up more often in L2.  The start depends only on
+// the tile, so a gathered (fused-dispatch) product and one reading xd sum in the same order.
+// At X-MoE Large, P = 32 cuts L2->fabric reads of the up product by about a quarter (19.7
+// -> 14.8 GB per launch) and the layer by 1-2%; keying the start on the dispatch position
+// instead measured the same; P = 16 and 64 read more and ran slower.  0 switches it off.
 #ifndef MOE_K_ROTATE
 #define MOE_K_ROTATE 32
 #endif
@@ -538,14 +549,15 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, 
         const int expert = te.x, first = te.y, seg0 = te.z, segn = te.w;
         const int n_e = (segn + BT - 1) / BT;
         const int q = L - p.feat_tiles * first;
-        const int blk_tiles = kGroupTok * p.feat_tiles;
-        const int blk = min(q / blk_tiles, (n_e - 1) / kGroupTok);
-        const int width = min(kGroupTok, n_e - blk * kGroupTok);
+        const int gtok = p.gather ? kGroupTokGather : kGroupTok;
+        const int blk_tiles = gtok * p.feat_tiles;
+        const int blk = min(q / blk_tiles, (n_e - 1) / gtok);
+        const int width = min(gtok, n_e - blk * gtok);
         const int ql = q - blk * blk_tiles;
         const int ftile = ql / width;
-        const int ttile = blk * kGroupTok + (ql - ftile * width);
+        const int ttile = blk * gtok + (ql - ftile * width);
         const int row0 = seg0 + ttile * BT, row_end = min(seg0 + segn, p.act_rows);
-        const int rot = kRotate ? (j % kRotPeriod) * nk / kRotPeriod : 0;
+        const int rot = kRotate ? ((ttile + 7 * ftile) % kRotPeriod) * nk / kRotPeriod : 0;
         if (row_end - row0 >= BT)
             compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot);
         else
