@@ -72,14 +72,16 @@ constexpr int kGroupTokDown = MOE_GROUP_TOK_DOWN;
 #define MOE_INTERLEAVE_READS 1
 #endif
 constexpr bool kInterleave = MOE_INTERLEAVE_READS != 0;
-// A large tile starts its K loop at slice ((ttile + 7 ftile) mod P) * nk / P and wraps
-// around (ttile, ftile: its token and feature tile within the expert).  Tiles that share an
-// operand panel and run at the same time then sit at different points of K, and as CUs free
-// up at different times their slices line up more often in L2.  The start depends only on
-// the tile, so a gathered (fused-dispatch) product and one reading xd sum in the same order.
-// At X-MoE Large, P = 32 cuts L2->fabric reads of the up product by about a quarter (19.7
-// -> 14.8 GB per launch) and the layer by 1-2%; keying the start on the dispatch position
-// instead measured the same; P = 16 and 64 read more and ran slower.  0 switches it off.
+// In a launch that also streams small experts' weights, a large tile starts its K loop at
+// slice ((ttile + 7 ftile) mod P) * nk / P and wraps around (ttile, ftile: its token and
+// feature tile within the expert).  There the large tiles start at staggered times as CUs
+// free up from tiles of unequal length, and tiles sharing an operand panel then line up
+// their slices in L2 more often; without small tiles, tiles start and run together and the
+// natural order shares best.  The start depends only on the tile, so a gathered
+// (fused-dispatch) product and one reading xd sum in the same order.  Measured (fused layer,
+// on / off): X-MoE Large 4.19 / 4.25 ms, X-MoE Super 5.27 / 5.33 ms; X-MoE Medium (no small
+// experts) 1.81 / 1.77 ms and dense products up to 30% slower with it, hence the
+// condition.  P = 16 and 64 read more and ran slower at X-MoE Large; 0 switches it off.
 #ifndef MOE_K_ROTATE
 #define MOE_K_ROTATE 32
 #endif
@@ -564,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, 
         const int ftile = ql / width;
         const int ttile = blk * gtok + (ql - ftile * width);
         const int row0 = seg0 + ttile * BT, row_end = min(seg0 + segn, p.act_rows);
-        const int rot = kRotate ? ((ttile + 7 * ftile) % kRotPeriod) * nk / kRotPeriod : 0;
+        const int rot = kRotate && tot_s > 0 ? ((ttile + 7 * ftile) % kRotPeriod) * nk / kRotPeriod : 0;
         if (row_end - row0 >= BT)
             compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot);
         else
