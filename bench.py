@@ -269,6 +269,8 @@ def main():
     alg = algorithmic(cfg, counts)
     g_ms = st_ms["grouped_gemm"]
     tflops = alg["gemm_flops"] / (g_ms * 1e-3) / 1e12
+    g_attain = min(MFMA_PEAK_TFLOPS[cfg.dtype],
+                   alg["gemm_flops"] / alg["gemm_bytes"] * HBM_PEAK_GBS * 1e9 / 1e12)
     up_tflops = alg["up_flops"] / (up_ms * 1e-3) / 1e12
     up_gbs = alg["up_bytes"] / (up_ms * 1e-3) / 1e9
     peak = MFMA_PEAK_TFLOPS[cfg.dtype]
@@ -348,7 +350,10 @@ def main():
                            "gbs": round(up_gbs, 1), "frac_hbm": round(up_gbs / HBM_PEAK_GBS, 4)},
             "source_sha256": kernel_digest()},
         "grouped_gemm": {"tflops": round(tflops, 2), "frac_mfma": round(tflops / peak, 4),
-                         "us": round(g_ms * 1e3, 1)},
+                         "us": round(g_ms * 1e3, 1),
+                         # the roofline bound at its arithmetic intensity: min(peak, AI x HBM)
+                         "attainable_tflops": round(g_attain, 1),
+                         "frac_attainable": round(tflops / g_attain, 4)},
         "stages_us": stage_report | {"up_kernel": round(up_ms * 1e3, 2)},
         "staged_layer": {"ms_per_step": round(staged_ms, 4),
                          "tokens_per_s": round(cfg.T / (staged_ms * 1e-3), 1),
