@@ -65,6 +65,9 @@ def parse():
                     help="only run plain device copies of 1 GiB (counter calibration)")
     ap.add_argument("--up-kernel-only", action="store_true",
                     help="one staged layer, then --steps calls of the up product alone")
+    ap.add_argument("--weight-stream", action="store_true",
+                    help="the up product on a routing of one row per expert for every expert of "
+                         "the workload: a pure stream of the expert weights (for counter runs)")
     return ap.parse_args()
 
 
@@ -171,6 +174,32 @@ def cpu_baseline(cfg, d, seed, target_s):
                       f"dispatch/experts/combine = {', '.join(f'{s:.2f}' for s in secs)}"}
 
 
+def weight_stream(cfg, args, dev):
+    """The up product with every expert given exactly one row: each expert's W1 and W3 are
+    read once and almost nothing else moves, so the launch is a pure weight stream through
+    the small-expert tiles.  Prints the streamed bytes per launch and the rate."""
+    import torch
+
+    from gemm_gate_softmax_amd import ops
+    from gemm_gate_softmax_amd import workloads as W
+
+    d = W.make_device(cfg, seed=args.seed, device=dev)
+    E, H, F = cfg.E, cfg.H, cfg.F
+    xd = d["x"][:E].contiguous()
+    offsets = torch.arange(0, E + 1, dtype=torch.int32, device=dev)
+    h = torch.empty((E, F), dtype=xd.dtype, device=dev)
+    ws = ops.workspace(ops.MOE_WS_GEMM, E, H, E, F, 1, ops.dtype_code(xd.dtype), dev)
+    call = lambda: ops.moe_grouped_gemm_swiglu(xd, offsets, d["w1"], d["w3"], None, h=h, ws=ws)
+    call()
+    torch.cuda.synchronize()
+    ms = time_calls(call, max(1, args.steps), torch.cuda.current_stream())
+    nbytes = E * 2.0 * F * H * xd.element_size()
+    print(json.dumps({"weight_stream": cfg.name, "experts": E, "bytes_per_launch": nbytes,
+                      "us": round(ms * 1e3, 1), "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -190,6 +219,8 @@ def main():
     cfg = W.CONFIGS[args.config]
     dev = "cuda"
     ops.lib()                                   # the HIP library or nothing
+    if args.weight_stream:
+        return weight_stream(cfg, args, dev)
     log(f"bench: {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} F={cfg.F} k={cfg.k} {cfg.dtype}: "
         "drawing inputs on the device")
     d = W.make_device(cfg, seed=args.seed, device=dev)
