@@ -349,12 +349,14 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
             _Pragma("unroll") for (int i = 0; i < FT; ++i) FW[b][i] = *reinterpret_cast<const uint4*>( \
                 st_ + (BT + b * BF + wf * (BF / 2) + i * 32 + l32) * kRowBytes + cs_);      \
     } while (0)
-    // Scheduling hint: one fragment read after each MFMA, so reads issue while the MFMA
-    // pipe is busy rather than as a block between two MFMA runs.
+    // Scheduling hint (bf16, one MFMA instruction per fragment pair): one fragment read after
+    // each MFMA, so reads issue while the MFMA pipe is busy rather than as a block between
+    // two MFMA runs.  (fp32 makes four MFMA instructions per pair; the hint cost it 1%.)
     constexpr int kMfmaPerStep = NB * FT * TT, kReadsPerStep = TT + NB * FT;
+    constexpr bool kHint = kInterleave && sizeof(T) == 2;
 #define MOE_INTERLEAVE()                                                                      \
     do {                                                                                     \
-        if constexpr (kInterleave) {                                                         \
+        if constexpr (kHint) {                                                               \
             _Pragma("unroll") for (int q_ = 0; q_ < kMfmaPerStep; ++q_) {                    \
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           \
                 if (q_ < kReadsPerStep) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   \
@@ -381,20 +383,20 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
 #pragma unroll
         for (int ks = 0; ks < KS; ks += 2) {
             MOE_LOAD_FRAGS(st, ks + 1, fa1, fw1);
-            if constexpr (!kInterleave) __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!kHint) __builtin_amdgcn_sched_barrier(0);
             MOE_MFMAS(fa0, fw0);
             MOE_INTERLEAVE();
             __builtin_amdgcn_sched_barrier(0);
             if (ks + 2 < KS) {
                 MOE_LOAD_FRAGS(st, ks + 2, fa0, fw0);
-                if constexpr (!kInterleave) __builtin_amdgcn_sched_barrier(0);
+                if constexpr (!kHint) __builtin_amdgcn_sched_barrier(0);
                 MOE_MFMAS(fa1, fw1);
                 MOE_INTERLEAVE();
             } else {
                 __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (3 << 14));   // lgkmcnt(0)
                 __builtin_amdgcn_s_barrier();                        // barrier kt+1
                 MOE_LOAD_FRAGS(lds + next * kStageBytes, 0, fa0, fw0);
-                if constexpr (!kInterleave) __builtin_amdgcn_sched_barrier(0);
+                if constexpr (!kHint) __builtin_amdgcn_sched_barrier(0);
                 MOE_MFMAS(fa1, fw1);
                 MOE_INTERLEAVE();
             }
