@@ -68,6 +68,7 @@ constexpr int kGroupTokGather = MOE_GROUP_TOK_GATHER;
 #define MOE_GROUP_TOK_DOWN 32
 #endif
 constexpr int kGroupTokDown = MOE_GROUP_TOK_DOWN;
+// bf16 tiles: scheduling hints place one fragment read after each MFMA (compute_tile)
 #ifndef MOE_INTERLEAVE_READS
 #define MOE_INTERLEAVE_READS 1
 #endif
