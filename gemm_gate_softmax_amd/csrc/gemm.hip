@@ -141,7 +141,16 @@ struct PickOut<true, T> {
     using type = float;
 };
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+#ifndef MOE_FAST_SILU
+#define MOE_FAST_SILU 1
+#endif
+// silu(a) = a / (1 + e^-a).  The fast form multiplies by the hardware reciprocal (1 ulp)
+// instead of an IEEE division (about ten instructions per output in every tile's
+// epilogue); h is rounded to the storage type right after.
+__device__ __forceinline__ float silu(float a) {
+    if constexpr (MOE_FAST_SILU) return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+    else return a / (1.0f + __expf(-a));
+}
 
 // One 16-byte global -> LDS transfer per lane, no register round trip (gfx950).  The LDS
 // destination of a wave's instruction is the 1 KiB block at byte address `lds_block`
