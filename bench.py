@@ -347,11 +347,27 @@ def main():
             d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k, bufs_f, dout,
             grads=grads, ws=bws), bsteps, stream)
         bflops = 16.0 * cfg.N * cfg.H * cfg.F
+        # The same with the forward storing the up product's halves a and g (bufs a, g), so
+        # the backward skips their recomputation; the forward that stores them is timed too.
+        bufs_t = ops.alloc_layer_bufs(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, d["x"].dtype, dev,
+                                      fuse_dispatch=True, store_ag=True)
+        fwd_ag = lambda: ops.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w3"],
+                                               d["w2"], cfg.k, out=out, bufs=bufs_t, ws=ws)
+        fwd_ag()
+        torch.cuda.synchronize()
+        fwd_ag_ms = time_calls(fwd_ag, bsteps, stream)
+        bwd_ag_ms = time_calls(lambda: ops.moe_layer_backward(
+            d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k, bufs_t, dout,
+            grads=grads, ws=bws), bsteps, stream)
         bwd = {"ms_per_step": round(bwd_ms, 3), "tokens_per_s": round(cfg.T / (bwd_ms * 1e-3), 1),
                "steps": bsteps, "tflops": round(bflops / (bwd_ms * 1e-3) / 1e12, 2),
                "workspace_GB": round(bws.numel() / 1e9, 2),
-               "note": "moe_layer_backward after the fused forward: dx, dWg, dbias, dW1, dW3, dW2"}
-        del grads, bws, dout
+               "note": "moe_layer_backward after the fused forward: dx, dWg, dbias, dW1, dW3, dW2",
+               "stored_ag": {"backward_ms": round(bwd_ag_ms, 3),
+                             "forward_ms": round(fwd_ag_ms, 4),
+                             "note": "forward storing a and g beside h; backward without "
+                                     "their recomputation"}}
+        del grads, bws, dout, bufs_t
         torch.cuda.empty_cache()
     if args.verbose:
         for n, v in st_ms.items():

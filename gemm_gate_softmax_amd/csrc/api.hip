@@ -181,6 +181,8 @@ MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int 
     MOE_TRY(check_ptrs({x, wg, w1, w3, w2, out, ws, b->top_experts, b->top_weights, b->counts,
                         b->offsets, b->token_ids, b->expert_ids, b->dest_pos, b->h, b->y}));
     if (b->xd && !aligned16(b->xd)) return MOE_ERR_MISALIGNED;
+    if ((b->a == nullptr) != (b->g == nullptr)) return MOE_ERR_INVALID_VALUE;
+    if (b->a && (!aligned16(b->a) || !aligned16(b->g))) return MOE_ERR_MISALIGNED;
     if (bias && !aligned16(bias)) return MOE_ERR_MISALIGNED;
     const size_t need_pft = pft_ws(T, k, E), need_gate = gate_ws(dt, T, H, E);
     const long long N = (long long)T * k;
@@ -198,11 +200,11 @@ MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int 
     if (b->xd) {
         MOE_TRY(launched(moe::launch_dispatch(dt, T, k, H, x, b->dest_pos, b->xd, s)));
         MOE_TRY(launched(moe::launch_grouped_gemm(dt, (int)N, E, H, F, b->xd, b->offsets, w1, w3,
-                                                  w2, b->h, b->y, ws_gemm, s)));
+                                                  w2, b->h, b->y, ws_gemm, s, b->a, b->g)));
     } else {  // dispatch fused into the expert product: rows gathered from x on load
         MOE_TRY(launched(moe::launch_grouped_gemm_gather(dt, (int)N, E, H, F, x, T, b->token_ids,
                                                          b->offsets, w1, w3, w2, b->h, b->y,
-                                                         ws_gemm, s)));
+                                                         ws_gemm, s, b->a, b->g)));
     }
     return launched(moe::launch_combine(dt, T, k, H, b->y, b->dest_pos, b->top_weights, out, s));
 }
@@ -223,6 +225,8 @@ MOE_API moe_status_t moe_layer_backward(moe_dtype_t dt, int T, int H, int E, int
                         fwd->top_experts, fwd->top_weights, fwd->counts, fwd->offsets,
                         fwd->token_ids, fwd->dest_pos, fwd->h, fwd->y}));
     if (fwd->xd && !aligned16(fwd->xd)) return MOE_ERR_MISALIGNED;
+    if ((fwd->a == nullptr) != (fwd->g == nullptr)) return MOE_ERR_INVALID_VALUE;
+    if (fwd->a && (!aligned16(fwd->a) || !aligned16(fwd->g))) return MOE_ERR_MISALIGNED;
     if (bias && !aligned16(bias)) return MOE_ERR_MISALIGNED;
     if (dtop_weights && !aligned16(dtop_weights)) return MOE_ERR_MISALIGNED;
     if (ws_bytes < round_up(moe::backward_ws_bytes(dt, T, H, E, F, k)))
@@ -233,6 +237,7 @@ MOE_API moe_status_t moe_layer_backward(moe_dtype_t dt, int T, int H, int E, int
     b.top_experts = fwd->top_experts; b.top_weights = fwd->top_weights;
     b.counts = fwd->counts; b.offsets = fwd->offsets; b.token_ids = fwd->token_ids;
     b.dest_pos = fwd->dest_pos; b.xd = fwd->xd; b.h = fwd->h; b.y = fwd->y; b.dout = dout;
+    b.a = fwd->a; b.g = fwd->g;
     b.dx = dx; b.dwg = dwg; b.dbias = dbias; b.dw1 = dw1; b.dw3 = dw3; b.dw2 = dw2;
     b.dtw = dtop_weights; b.ws = ws;
     return launched(moe::launch_layer_backward(b, as_stream(stream)));

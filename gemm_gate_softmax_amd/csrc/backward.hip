@@ -537,13 +537,17 @@ hipError_t layer_backward_t(const BwdParams& b, hipStream_t s) {
                                 w.gemm, s));
     const void* act = b.xd ? b.xd : b.x;
     const int32_t* gather = b.xd ? nullptr : b.token_ids;
-    MOE_CHECK(launch_grouped_pair(dt, N, E, H, F, act, gather, T_, b.offsets, b.w1, b.w3, w.a, w.g,
-                                  w.gemm, s));
+    // a and g: stored by the forward, or recomputed (the same tiles and summation order)
+    const void* ag_a = b.a ? b.a : w.a;
+    const void* ag_g = b.g ? b.g : w.g;
+    if (!b.a)
+        MOE_CHECK(launch_grouped_pair(dt, N, E, H, F, act, gather, T_, b.offsets, b.w1, b.w3, w.a,
+                                      w.g, w.gemm, s));
     const int fchunks = (int)((size_t)F * sizeof(T) / 16);
     const long long nfc = (long long)N * fchunks;
     hipLaunchKernelGGL(swiglu_bwd_kernel<T>, dim3((unsigned)((nfc + 255) / 256)), dim3(256), 0, s,
-                       static_cast<const uint4*>(w.dh), static_cast<const uint4*>(w.a),
-                       static_cast<const uint4*>(w.g), nfc, fchunks, static_cast<uint4*>(w.dag));
+                       static_cast<const uint4*>(w.dh), static_cast<const uint4*>(ag_a),
+                       static_cast<const uint4*>(ag_g), nfc, fchunks, static_cast<uint4*>(w.dag));
     MOE_CHECK(hipGetLastError());
     MOE_CHECK(launch_grouped_nt(dt, N, E, 2 * F, H, w.dag, b.offsets, w.w13t,
                                 (long long)H * 2 * F, w.dxd, w.gemm, s));

@@ -28,8 +28,10 @@ namespace {
 
 constexpr int kThreads = 512;   // 4 compute waves + 4 loader waves
 
-// kEpiPair (NB = 2) stores both products, a to out and g to out2 (the backward needs them).
-enum Epilogue { kEpiLogits = 0, kEpiSwiGLU = 1, kEpiStore = 2, kEpiPair = 3 };
+// kEpiPair (NB = 2) stores both products, a to out and g to out2 (the backward needs them);
+// kEpiSwiGLUPair stores h = silu(a) * g to out and also a to out2, g to out3 (a forward whose
+// backward is to follow).
+enum Epilogue { kEpiLogits = 0, kEpiSwiGLU = 1, kEpiStore = 2, kEpiPair = 3, kEpiSwiGLUPair = 4 };
 
 // Tile shapes.  Expert products: 128 tokens; up product 128 features x 2 operands, down
 // product 256 features; a 3-slot ring of 48 KiB k-slices (64 k per row, whole 128-byte
@@ -116,7 +118,8 @@ struct GemmParams {
     const int* table_count; // [0] entries in table, [1] entries in stable
     int dense_rows;         // rows of the single expert of a dense product (gate)
     void* out;              // [rows][n_feat]: fp32 partial logits or storage type
-    void* out2;             // kEpiPair: the second operand's product
+    void* out2;             // kEpiPair: the second operand's product; kEpiSwiGLUPair: a
+    void* out3;             // kEpiSwiGLUPair: g
     int k_slices;           // dense product: k-slices per K split
     int group_tok;          // expert product: token tiles per L2-sharing block (0: kGroupTok)
 };
@@ -463,11 +466,11 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
     }
     char* stg = lds + wave * (BT / 2) * kPitch;
     const int tok0 = row0 + wt * (BT / 2), feat0 = f0 + wf * (BF / 2);
-    constexpr int kOuts = EPI == kEpiPair ? 2 : 1;
+    constexpr int kOuts = EPI == kEpiPair ? 2 : (EPI == kEpiSwiGLUPair ? 3 : 1);
 #pragma unroll
     for (int ob = 0; ob < kOuts; ++ob) {
-        // (one wave's LDS operations run in order, so the second pass's writes come after
-        // the first pass's reads of the same region)
+        // (one wave's LDS operations run in order, so a pass's writes come after the
+        // previous pass's reads of the same region)
 #pragma unroll
         for (int i = 0; i < FT; ++i) {
 #pragma unroll
@@ -477,9 +480,12 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
                     float r[4];
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const float a = acc[ob][i][j][4 * g + v];
-                        if constexpr (EPI == kEpiSwiGLU) r[v] = silu(a) * acc[NB - 1][i][j][4 * g + v];
-                        else r[v] = a;
+                        if constexpr (EPI == kEpiSwiGLU || EPI == kEpiSwiGLUPair) {
+                            if (ob == 0) r[v] = silu(acc[0][i][j][4 * g + v]) * acc[NB - 1][i][j][4 * g + v];
+                            else r[v] = acc[ob - 1][i][j][4 * g + v];
+                        } else {
+                            r[v] = acc[ob][i][j][4 * g + v];
+                        }
                     }
                     char* dst = stg + (j * 32 + l32) * kPitch + (i * 32 + 8 * g + 4 * lhalf) * (int)sizeof(OutT);
                     if constexpr (sizeof(OutT) == 4) {
@@ -492,7 +498,7 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
                 }
             }
         }
-        OutT* out = static_cast<OutT*>(ob == 0 ? p.out : p.out2);
+        OutT* out = static_cast<OutT*>(ob == 0 ? p.out : (ob == 1 ? p.out2 : p.out3));
 #pragma unroll
         for (int k = 0; k < kOutChunks / 64; ++k) {
             const int c = lane + 64 * k;
@@ -712,7 +718,8 @@ inline TableLayout carve_tables(void* ws, int N, int E) {
 template <typename T>
 hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* gather,
                      int src_rows, const int32_t* offsets, const void* w1, const void* w3,
-                     const void* w2, void* h, void* y, void* ws, hipStream_t s) {
+                     const void* w2, void* h, void* y, void* a, void* g, void* ws,
+                     hipStream_t s) {
     constexpr int BT = kExpertBTok;
     const TableLayout tl = carve_tables(ws, N, E);
     hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, N, BT, kSmallBTok,
@@ -738,8 +745,14 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
     up.stable = tl.stable;
     up.table_count = tl.count;
     up.out = h;
-    err = launch_expert<T, 2, kEpiSwiGLU, BT, UP_BF, STAGES, RB>(
-        up, tl.cap * up.feat_tiles, max_small * up.feat_tiles, s);
+    up.out2 = a;
+    up.out3 = g;
+    if (a != nullptr && g != nullptr)
+        err = launch_expert<T, 2, kEpiSwiGLUPair, BT, UP_BF, STAGES, RB>(
+            up, tl.cap * up.feat_tiles, max_small * up.feat_tiles, s);
+    else
+        err = launch_expert<T, 2, kEpiSwiGLU, BT, UP_BF, STAGES, RB>(
+            up, tl.cap * up.feat_tiles, max_small * up.feat_tiles, s);
     if (err != hipSuccess || w2 == nullptr) return err;      // up product only
 
     GemmParams<T, 1> dn{};
@@ -913,19 +926,20 @@ hipError_t launch_gate_logits(int dt, int T, int H, int E, const void* x, const 
 
 hipError_t launch_grouped_gemm(int dt, int N, int E, int H, int F, const void* xd,
                                const int32_t* offsets, const void* w1, const void* w3,
-                               const void* w2, void* h, void* y, void* ws, hipStream_t s) {
+                               const void* w2, void* h, void* y, void* ws, hipStream_t s,
+                               void* a, void* g) {
     if (N == 0) return hipSuccess;
-    return dt == 0 ? grouped_t<float>(N, E, H, F, xd, nullptr, 0, offsets, w1, w3, w2, h, y, ws, s)
-                   : grouped_t<bf16_t>(N, E, H, F, xd, nullptr, 0, offsets, w1, w3, w2, h, y, ws, s);
+    return dt == 0 ? grouped_t<float>(N, E, H, F, xd, nullptr, 0, offsets, w1, w3, w2, h, y, a, g, ws, s)
+                   : grouped_t<bf16_t>(N, E, H, F, xd, nullptr, 0, offsets, w1, w3, w2, h, y, a, g, ws, s);
 }
 
 hipError_t launch_grouped_gemm_gather(int dt, int N, int E, int H, int F, const void* x, int T,
                                       const int32_t* token_ids, const int32_t* offsets,
                                       const void* w1, const void* w3, const void* w2, void* h,
-                                      void* y, void* ws, hipStream_t s) {
+                                      void* y, void* ws, hipStream_t s, void* a, void* g) {
     if (N == 0) return hipSuccess;
-    return dt == 0 ? grouped_t<float>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, ws, s)
-                   : grouped_t<bf16_t>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, ws, s);
+    return dt == 0 ? grouped_t<float>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, a, g, ws, s)
+                   : grouped_t<bf16_t>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, a, g, ws, s);
 }
 
 hipError_t launch_grouped_nt(int dt, int N, int E, int K, int n_feat, const void* act,

@@ -30,15 +30,18 @@ hipError_t launch_combine(int dt, int T, int k, int H, const void* y, const int3
                           const float* top_weights, void* out, hipStream_t s);
 
 size_t gemm_ws_bytes(long long N, int E);
+// a, g (both or neither, [N][F] each): the up product's two halves are stored beside h.
 hipError_t launch_grouped_gemm(int dt, int N, int E, int H, int F, const void* xd,
                                const int32_t* offsets, const void* w1, const void* w3,
-                               const void* w2, void* h, void* y, void* ws, hipStream_t s);
+                               const void* w2, void* h, void* y, void* ws, hipStream_t s,
+                               void* a = nullptr, void* g = nullptr);
 // The same product with the dispatch fused in: row p of the up product reads x[token_ids[p]]
 // (x has T rows) instead of xd[p]; nothing is written for xd.
 hipError_t launch_grouped_gemm_gather(int dt, int N, int E, int H, int F, const void* x, int T,
                                       const int32_t* token_ids, const int32_t* offsets,
                                       const void* w1, const void* w3, const void* w2, void* h,
-                                      void* y, void* ws, hipStream_t s);
+                                      void* y, void* ws, hipStream_t s, void* a = nullptr,
+                                      void* g = nullptr);
 
 // ---- backward ----
 // out[p][f] = sum_k act[p][k] * w[e][f][k] over the expert segments (w advances w_stride
@@ -68,6 +71,7 @@ struct BwdParams {
     const float* top_weights;
     const int32_t *counts, *offsets, *token_ids, *dest_pos;
     const void *xd, *h, *y, *dout;      // xd may be NULL (rows gathered from x)
+    const void *a, *g;                  // the forward's stored up-product halves, or NULL
     void *dx, *dwg;
     float* dbias;
     void *dw1, *dw3, *dw2;

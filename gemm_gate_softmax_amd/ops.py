@@ -38,7 +38,7 @@ class LayerBufs(ctypes.Structure):
     """Mirror of ``moe_layer_bufs``."""
     _fields_ = [(n, ctypes.c_void_p) for n in ("top_experts", "top_weights", "counts", "offsets",
                                                "token_ids", "expert_ids", "dest_pos", "xd", "h",
-                                               "y")]
+                                               "y", "a", "g")]
 
 
 _lib = None
@@ -234,12 +234,15 @@ def moe_combine(y, dest_pos, top_weights, out=None, stream=None):
     return out
 
 
-def alloc_layer_bufs(T, H, E, F, k, dtype, device, fuse_dispatch=False) -> dict:
+def alloc_layer_bufs(T, H, E, F, k, dtype, device, fuse_dispatch=False, store_ag=False) -> dict:
     """Intermediates of moe_layer_forward.  fuse_dispatch=True leaves xd out (None): the
-    layer then gathers the expert rows from x on load and never writes xd."""
+    layer then gathers the expert rows from x on load and never writes xd.  store_ag=True
+    adds a and g [N,F]: the forward then stores the up product's two halves, which
+    moe_layer_backward uses instead of recomputing them."""
     N = T * k
     i32 = dict(dtype=torch.int32, device=device)
-    return dict(top_experts=torch.empty((T, k), **i32),
+    ag = (lambda: torch.empty((N, F), dtype=dtype, device=device)) if store_ag else (lambda: None)
+    return dict(a=ag(), g=ag(), top_experts=torch.empty((T, k), **i32),
                 top_weights=torch.empty((T, k), dtype=torch.float32, device=device),
                 counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
                 token_ids=torch.empty(N, **i32), expert_ids=torch.empty(N, **i32),
@@ -247,6 +250,13 @@ def alloc_layer_bufs(T, H, E, F, k, dtype, device, fuse_dispatch=False) -> dict:
                 xd=None if fuse_dispatch else torch.empty((N, H), dtype=dtype, device=device),
                 h=torch.empty((N, F), dtype=dtype, device=device),
                 y=torch.empty((N, H), dtype=dtype, device=device))
+
+
+def _need_ag(bufs, N, F, dtype):
+    # a and g come together or not at all (the C side rejects one alone as well)
+    for n in ("a", "g"):
+        if bufs.get(n) is not None:
+            _need(bufs[n], n, dtype, (N, F))
 
 
 def moe_layer_forward(x, wg, bias, w1, w3, w2, k, out=None, bufs=None, ws=None, stream=None,
@@ -266,7 +276,8 @@ def moe_layer_forward(x, wg, bias, w1, w3, w2, k, out=None, bufs=None, ws=None, 
     if bufs is None:
         bufs = alloc_layer_bufs(T, H, E, F, k, x.dtype, x.device, fuse_dispatch)
     ws = workspace(MOE_WS_LAYER, T, H, E, F, k, dt, x.device) if ws is None else ws
-    cb = LayerBufs(*[_ptr(bufs[n]) for n, _ in LayerBufs._fields_])
+    _need_ag(bufs, T * k, F, x.dtype)
+    cb = LayerBufs(*[_ptr(bufs.get(n)) for n, _ in LayerBufs._fields_])
     _check("moe_layer_forward", lib().moe_layer_forward(
         dt, T, H, E, F, k, ROUTING[routing], _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3),
         _ptr(w2), _ptr(out),
@@ -296,7 +307,8 @@ def moe_layer_backward(x, wg, bias, w1, w3, w2, k, bufs, dout, grads=None, ws=No
                      dw2=torch.empty((E, H, F), dtype=x.dtype, device=dev),
                      dtw=torch.empty((T, k), dtype=torch.float32, device=dev))
     ws = workspace(MOE_WS_BACKWARD, T, H, E, F, k, dt, x.device) if ws is None else ws
-    cb = LayerBufs(*[_ptr(bufs[n]) for n, _ in LayerBufs._fields_])
+    _need_ag(bufs, T * k, F, x.dtype)
+    cb = LayerBufs(*[_ptr(bufs.get(n)) for n, _ in LayerBufs._fields_])
     _check("moe_layer_backward", lib().moe_layer_backward(
         dt, T, H, E, F, k, ROUTING[routing], _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3),
         _ptr(w2), ctypes.byref(cb), _ptr(dout), _ptr(grads["dx"]), _ptr(grads["dwg"]),

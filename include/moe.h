@@ -175,6 +175,8 @@ typedef struct moe_layer_bufs {
     void *xd;             /* [N][H], or NULL (dispatch fused into the experts) */
     void *h;              /* [N][F] */
     void *y;              /* [N][H] */
+    void *a;              /* [N][F] or NULL: a = xd.W1[e]^T, stored by the forward when a and g */
+    void *g;              /* [N][F] or NULL: g = xd.W3[e]^T  are both set (for the backward)   */
 } moe_layer_bufs;
 
 /*

@@ -142,6 +142,10 @@ def test_gemm_and_layer_reject(L):
     assert lf(*args(bufs=xb)) == MISALIGNED
     nb7 = ops.LayerBufs(*([A] * 6 + [None, None, A, A]))  # dest_pos stays required
     assert lf(*args(bufs=nb7)) == INVALID
+    # the up product's halves a and g: both or neither, aligned
+    assert lf(*args(bufs=ops.LayerBufs(*([A] * 10 + [A, None])))) == INVALID
+    assert lf(*args(bufs=ops.LayerBufs(*([A] * 10 + [None, A])))) == INVALID
+    assert lf(*args(bufs=ops.LayerBufs(*([A] * 10 + [MIS, A])))) == MISALIGNED
     assert lf(*args(T=0)) == OK
 
 
@@ -164,6 +168,8 @@ def test_layer_backward_rejects(L):
     assert lb(*args(bufs=nh)) == INVALID
     xb = ops.LayerBufs(*([A] * 7 + [MIS, A, A]))        # xd may be NULL, never misaligned
     assert lb(*args(bufs=xb)) == MISALIGNED
+    assert lb(*args(bufs=ops.LayerBufs(*([A] * 10 + [A, None])))) == INVALID   # a without g
+    assert lb(*args(bufs=ops.LayerBufs(*([A] * 10 + [A, MIS])))) == MISALIGNED
     assert lb(*args(T=0)) == OK
 
 

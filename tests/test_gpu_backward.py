@@ -103,6 +103,39 @@ def test_backward_fused_and_staged_identical_and_deterministic(dt):
         assert torch.equal(g1[n], g3[n]), n
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("fuse", [True, False])
+def test_backward_with_stored_up_halves_identical(dt, fuse):
+    """The forward can store a = x.W1^T and g = x.W3^T beside h (bufs a and g); the backward
+    then uses them instead of recomputing them on the same tiles in the same order, so the
+    forward's outputs and every gradient are bit-identical either way."""
+    cfg = W.LayerConfig("small", T=300, H=256, E=16, F=192, k=4, dtype=dt, bias=("zipf", 1.2))
+    d = W.make_device(cfg, seed=0, device=DEV)
+    rng = np.random.default_rng(100)
+    dout = W.to_device(W._store(rng.standard_normal((cfg.T, cfg.H)), cfg.dtype), cfg.dtype, DEV)
+    args = (d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k)
+    results = []
+    for store in (False, True):
+        bufs = ops.alloc_layer_bufs(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, d["x"].dtype, DEV,
+                                    fuse_dispatch=fuse, store_ag=store)
+        out, bufs, _ = ops.moe_layer_forward(*args, bufs=bufs)
+        grads, _ = ops.moe_layer_backward(*args, bufs, dout)
+        torch.cuda.synchronize()
+        results.append((out, bufs, grads))
+    (o0, b0, g0), (o1, b1, g1) = results
+    assert torch.equal(o0, o1)
+    for n in ("h", "y", "top_experts", "top_weights", "token_ids", "dest_pos"):
+        assert torch.equal(b0[n], b1[n]), n
+    for n in GRADS:
+        assert torch.equal(g0[n], g1[n]), n
+    # the stored halves give back h: silu(a) * g rounded like h (tolerance: GPU exp and
+    # reciprocal against torch's)
+    a, g = b1["a"].double(), b1["g"].double()
+    h_ref = (a / (1.0 + torch.exp(-a)) * g)
+    err = ((b1["h"].double() - h_ref).abs().max() / h_ref.abs().max()).item()
+    assert err <= (1e-5 if dt == "f32" else 1e-2), err
+
+
 def test_experts_without_rows_get_zero_weight_gradients():
     cfg = W.LayerConfig("skewed", T=64, H=128, E=32, F=128, k=2, dtype="bf16", bias=("zipf", 2.0))
     _, _, bufs, grads = _run(cfg, "softmax", fuse=True)
