@@ -284,6 +284,49 @@ def test_layer_parity_small(orc, cfg):
     assert int(host(ws[:4].view(torch.int32))[0]) == 0
 
 
+# The method's degenerate layers: one expert (every token to it with weight 1: a dense
+# SwiGLU FFN), every expert chosen by every token (k = E), and a single token.
+DEGENERATE_LAYERS = [
+    W.LayerConfig("one_expert_f32", T=130, H=128, E=1, F=192, k=1, dtype="f32"),
+    W.LayerConfig("one_expert_bf16", T=300, H=192, E=1, F=128, k=1, dtype="bf16"),
+    W.LayerConfig("k_equals_e_bf16", T=100, H=192, E=8, F=128, k=8, dtype="bf16", bias=("zipf", 1.0)),
+    W.LayerConfig("one_token_bf16", T=1, H=256, E=64, F=128, k=6, dtype="bf16", bias=("zipf", 1.2)),
+]
+
+
+@pytest.mark.parametrize("cfg", DEGENERATE_LAYERS, ids=lambda c: c.name)
+def test_layer_degenerate_cases(orc, cfg):
+    d = W.make_host(cfg, seed=4)
+    dt = cfg.dtype
+    ref = orc.layer_forward(dt, d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k)
+    outs = []
+    for fuse in (False, True):
+        out, bufs, ws = ops.moe_layer_forward(dev(d["x"], dt), dev(d["wg"], dt), dev(d["bias"]),
+                                              dev(d["w1"], dt), dev(d["w3"], dt), dev(d["w2"], dt),
+                                              cfg.k, fuse_dispatch=fuse)
+        outs.append(out)
+        assert int(host(ws[:4].view(torch.int32))[0]) == 0
+        counts = host(bufs["counts"])
+        assert int(counts.sum()) == cfg.T * cfg.k
+        if cfg.k == cfg.E:             # every token picks every expert exactly once
+            assert np.array_equal(counts, np.full(cfg.E, cfg.T))
+            assert np.array_equal(np.sort(host(bufs["top_experts"]), axis=1),
+                                  np.tile(np.arange(cfg.E), (cfg.T, 1)))
+        if cfg.E == 1:                 # the renormalised weight of a single pick is exactly 1
+            assert np.all(host(bufs["top_weights"]) == 1.0)
+    assert torch.equal(outs[0], outs[1])
+    got = host(outs[0], dt)
+    err = max_abs_rel(got, ref, dt)
+    _log(f"layer {cfg.name}: err {err:.2e}")
+    assert err <= TOL[dt]
+    if cfg.E == 1 and dt == "f32":
+        # pinned apart from the oracle: the dense SwiGLU FFN by torch on the CPU (float64)
+        x = torch.from_numpy(np.asarray(d["x"], dtype=np.float64))
+        w1, w3, w2 = (torch.from_numpy(np.asarray(d[n][0], dtype=np.float64)) for n in ("w1", "w3", "w2"))
+        ffn = (torch.nn.functional.silu(x @ w1.T) * (x @ w3.T)) @ w2.T
+        assert max_abs_rel(got, ffn.numpy(), dt) <= TOL[dt]
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("T,H,E,k", [(200, 256, 8, 2), (333, 512, 64, 6), (256, 1024, 256, 8)])
 def test_gate_sigmoid_parity(orc, dt, T, H, E, k):
