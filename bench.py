@@ -324,6 +324,17 @@ def main():
     copy_ms = time_calls(lambda: cp_dst.copy_(cp_src), 10, stream)
     copy_gbs = 2.0 * cp_src.numel() / (copy_ms * 1e-3) / 1e9
     del cp_src, cp_dst
+    # launch floor for the buffer build (three kernels: histogram, scan, scatter): the same
+    # number of one-element fill kernels back to back on the same stream, timed the same way
+    tiny = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def chain3():
+        tiny.fill_(0)
+        tiny.fill_(1)
+        tiny.fill_(2)
+    chain3()
+    torch.cuda.synchronize()
+    floor_us = time_calls(chain3, args.steps, stream) * 1e3
     bw = {
         "copy_GBs": copy_gbs,
         "dispatch_GBs": alg["dispatch_bytes"] / (st_ms["dispatch"] * 1e-3) / 1e9,
@@ -402,6 +413,9 @@ def main():
                          "attainable_tflops": round(g_attain, 1),
                          "frac_attainable": round(tflops / g_attain, 4)},
         "stages_us": stage_report | {"up_kernel": round(up_ms * 1e3, 2)},
+        "buffers_vs_launch_floor": {"buffers_us": stage_report["buffers"],
+                                    "floor_us": round(floor_us, 2), "kernels": 3,
+                                    "ratio": round(stage_report["buffers"] / floor_us, 2)},
         "staged_layer": {"ms_per_step": round(staged_ms, 4),
                          "tokens_per_s": round(cfg.T / (staged_ms * 1e-3), 1),
                          "note": "dispatch as its own kernel (xd written and read back)"},
