@@ -279,10 +279,10 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
         }
         const uint32_t wbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
                                    (__attribute__((address_space(3))) char*)(lds))) + lw * 1024;
-        // all of stage KT into slot SLOT (4 loaders x 1 KiB per 4 KiB block).  Stage indices
-        // are clamped to the last stage, so every iteration issues the same transfers (a
-        // redundant copy lands in a slot no later stage reads) and every wait is constant.
-        // A tile that is not FULL transfers only the activation-row blocks holding a row
+        // all of stage KT into slot SLOT (4 loaders x 1 KiB per 4 KiB block).  Once every
+        // stage has been issued, the remaining iterations issue nothing and wait for fewer
+        // outstanding transfers (only a K range shorter than the ring issues clamped
+        // copies of the last stage up front).  A tile that is not FULL transfers only the activation-row blocks holding a row
         // below row_end (the vector-memory path is limited by cache-line requests, and an
         // expert with a handful of rows would otherwise move mostly duplicate rows).  The
         // skipped rows' LDS holds stale data that only ever meets the MFMA columns of
@@ -314,14 +314,21 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
         }
         int refill = S - 1;
         for (int kt = 0; kt < nk - 1; ++kt) {
-            MOE_ISSUE(min(kt + S - 1, nk - 1), refill);             // slot of stage kt-1
             // barrier kt+1: stage kt+1 landed
-            if constexpr (FULL) wait_vm_and_barrier<(S - 2) * kDma, false>();
-            else wait_vm_and_barrier_rt<(S - 2) * (kDma - kActDma), (S - 2) * kDma>((S - 2) * keff);
+            if (kt + S - 1 < nk) {
+                MOE_ISSUE(kt + S - 1, refill);                      // slot of stage kt-1
+                if constexpr (FULL) wait_vm_and_barrier<(S - 2) * kDma, false>();
+                else wait_vm_and_barrier_rt<(S - 2) * (kDma - kActDma), (S - 2) * kDma>((S - 2) * keff);
+            } else if constexpr (S == 3) {
+                wait_vm_and_barrier<0, false>();                     // nothing issued after kt+1
+            } else {
+                // the nk-2-kt (< S-2) stages after kt+1 may still be in flight
+                wait_vm_and_barrier_rt<0, (S - 3) * kDma>((nk - 2 - kt) * (FULL ? kDma : keff));
+            }
             refill = refill == S - 1 ? 0 : refill + 1;
         }
 #undef MOE_ISSUE
-        // redundant copies may still be landing; the workgroup's LDS must be quiet first
+        // (every transfer has landed: the last wait above was for none outstanding)
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));           // vmcnt(0)
         __builtin_amdgcn_s_barrier();                               // ring free: staging
         return;
