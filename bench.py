@@ -389,7 +389,8 @@ def main():
             f"{bw['dispatch_GBs']:.0f} GB/s, combine {bw['combine_GBs']:.0f} GB/s")
 
     rec = {
-        "metric": METRIC, "value": cfg.T / (ms_events * 1e-3), "unit": "tokens/s",
+        "metric": METRIC if cfg.name == "xmoe_large" else METRIC.replace("X-MoE Large", cfg.name),
+        "value": cfg.T / (ms_events * 1e-3), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_events, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
