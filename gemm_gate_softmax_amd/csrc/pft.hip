@@ -73,28 +73,45 @@ __global__ __launch_bounds__(kEMax) void pft_scan_kernel(int E, int nseg, int32_
                                                          int32_t* offsets, PftWs w) {
     constexpr int kBatch = 16;
     __shared__ int scan[2][kEMax];
+    __shared__ int bad[kEMax];
     const int e = threadIdx.x;
+    // out-of-range ids: a strided partial sum of the per-segment counts per thread, summed
+    // over the block in the scan's steps below
+    int my_bad = 0;
+    for (int s = e; s < nseg; s += kEMax) my_bad += w.seg_err[s];
     int run = 0;
     if (e < E) {
         for (int s0 = 0; s0 < nseg; s0 += kBatch) {
             int v[kBatch];
+            if (s0 + kBatch <= nseg) {           // a whole batch: the loads issue together
 #pragma unroll
-            for (int b = 0; b < kBatch; ++b)
-                v[b] = s0 + b < nseg ? w.hist[(size_t)(s0 + b) * E + e] : 0;
+                for (int b = 0; b < kBatch; ++b) v[b] = w.hist[(size_t)(s0 + b) * E + e];
 #pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                if (s0 + b < nseg) w.hist[(size_t)(s0 + b) * E + e] = run;
-                run += v[b];
+                for (int b = 0; b < kBatch; ++b) {
+                    w.hist[(size_t)(s0 + b) * E + e] = run;
+                    run += v[b];
+                }
+            } else {
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+                    v[b] = s0 + b < nseg ? w.hist[(size_t)(s0 + b) * E + e] : 0;
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b) {
+                    if (s0 + b < nseg) w.hist[(size_t)(s0 + b) * E + e] = run;
+                    run += v[b];
+                }
             }
         }
         counts[e] = run;
     }
     int cur = 0;
     scan[0][e] = run;
+    bad[e] = my_bad;
     __syncthreads();
     for (int d = 1; d < kEMax; d <<= 1) {
         const int v = scan[cur][e] + (e >= d ? scan[cur][e - d] : 0);
         scan[cur ^ 1][e] = v;
+        if ((e & (2 * d - 1)) == 0) bad[e] += bad[e + d];    // tree sum: bad[0] at the end
         cur ^= 1;
         __syncthreads();
     }
@@ -104,11 +121,7 @@ __global__ __launch_bounds__(kEMax) void pft_scan_kernel(int E, int nseg, int32_
         offsets[e] = base;
         if (e == E - 1) offsets[E] = incl;
     }
-    if (e == 0) {
-        int bad = 0;
-        for (int s = 0; s < nseg; ++s) bad += w.seg_err[s];
-        *w.err = bad;
-    }
+    if (e == 0) *w.err = bad[0];
 }
 
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void pft_scatter_kernel(
