@@ -78,6 +78,33 @@ def test_pft_deterministic_and_out_of_range(orc):
     assert dp[10, 3] == -1 and dp[2000, 0] == -1 and dp[2999, 7] == -1
 
 
+def test_pft_many_segments(orc):
+    # more routing entries than the scan's block has threads x 512 (one segment per wave of
+    # 512 entries): the per-expert running sums and the error count each take more than
+    # one segment per thread
+    rng = np.random.default_rng(11)
+    T, k, E = 140000, 4, 64
+    te = skewed_routing(rng, T, k, E, alpha=1.2)
+    assert (T * k + 511) // 512 > 1024
+    ref = orc.pft_build(te, E)
+    got = ops.moe_pft_build(dev(te), E)
+    torch.cuda.synchronize()
+    assert int(host(got["ws"][:4].view(torch.int32))[0]) == 0
+    for n in ("counts", "offsets", "token_ids", "expert_ids", "dest_pos"):
+        assert np.array_equal(host(got[n]), ref[n]), n
+    # out-of-range ids in the first segment and around and past segment 1024
+    bad = te.copy()
+    flat = [7, 1023 * 512 + 100, 1024 * 512 + 5, T * k - 1]
+    for i in flat:
+        bad[i // k, i % k] = E + i % 3
+    got = ops.moe_pft_build(dev(bad), E)
+    torch.cuda.synchronize()
+    assert int(host(got["ws"][:4].view(torch.int32))[0]) == len(flat)
+    dp = host(got["dest_pos"])
+    assert all(dp[i // k, i % k] == -1 for i in flat)
+    assert int(host(got["counts"]).sum()) == T * k - len(flat)
+
+
 # ---------------------------------------------------------------- dispatch / combine
 
 MOVE_SHAPES = [(1, 1, 64), (300, 3, 192), (4096, 8, 7168), (513, 6, 2048)]
