@@ -1,0 +1,76 @@
+"""Host-side tools around the benchmark (CPU only): the single-GPU guard of bench.py and the
+counter summaries whose HBM-traffic figure bench.py reports only while the kernel sources
+still hash to what was profiled."""
+import argparse
+import csv
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from gemm_gate_softmax_amd import profile_summary as ps  # noqa: E402
+
+
+def _csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+    return str(path)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_code_digest_ignores_comments_and_layout():
+    a = "int f(int x) {  // the value\n  return x /* doubled */ * 2;\n}\n"
+    b = "int f(int x) {\n\n    return x * 2;   }"
+    assert ps._code_only(a) == ps._code_only(b)
+    assert ps._code_only(a) != ps._code_only(a.replace("* 2", "* 3"))
+
+
+def _traffic_files(tmp_path, kernel):
+    # three dispatches of the kernel (1000 KiB fetched, 500 KiB written each) among others,
+    # and a 1 GiB copy whose FETCH_SIZE reads half its bytes and WRITE_SIZE all of them
+    fetch = _csv(tmp_path / "f.csv", [
+        {"Kernel_Name": kernel + "<x>(args)", "Dispatch_Id": d, "Counter_Value": v}
+        for d, v in ((1, 600), (1, 400), (2, 1000), (3, 1000))] +
+        [{"Kernel_Name": "other_kernel(int)", "Dispatch_Id": 9, "Counter_Value": 77}])
+    write = _csv(tmp_path / "w.csv", [
+        {"Kernel_Name": kernel + "<x>(args)", "Dispatch_Id": d, "Counter_Value": 500}
+        for d in (1, 2, 3)])
+    cf = _csv(tmp_path / "cf.csv", [{"Kernel_Name": "copy", "Dispatch_Id": 1, "Counter_Value": 524288},
+                                     {"Kernel_Name": "fill", "Dispatch_Id": 2, "Counter_Value": 3}])
+    cw = _csv(tmp_path / "cw.csv", [{"Kernel_Name": "copy", "Dispatch_Id": 1, "Counter_Value": 1048576}])
+    return argparse.Namespace(kernel=kernel, workload="synthetic_case", fetch=fetch, write=write,
+                              copy_fetch=cf, copy_write=cw, copy_bytes=1 << 30,
+                              command=["rocprofv3 --pmc FETCH_SIZE -- python3 bench.py"])
+
+
+def test_traffic_summary_scales_by_the_copy_and_is_tied_to_the_sources(tmp_path, monkeypatch):
+    a = _traffic_files(tmp_path, "expert_gemm_kernel")
+    md = tmp_path / "traffic.md"
+    md.write_text(ps.traffic_markdown(a))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(md))
+    # fetch: 1000 KiB x 1024 x (2^30 / (524288 KiB x 1024)) = 2,048,000 bytes; write 512,000
+    assert bench.recorded_traffic("synthetic_case") == 2048000 + 512000
+    assert bench.recorded_traffic("another_workload") is None
+    monkeypatch.setattr(bench, "kernel_digest", lambda: "0" * 16)
+    assert bench.recorded_traffic("synthetic_case") is None
+
+
+def test_last_dispatches_of_a_kernel(tmp_path):
+    trace = _csv(tmp_path / "t.csv", [
+        {"Kernel_Name": name, "Start_Timestamp": s, "End_Timestamp": s + d}
+        for name, s, d in (("k_a<1>(int)", 100, 5000), ("k_b(int)", 200, 9000),
+                           ("k_a<1>(int)", 300, 7000), ("k_a<1>(int)", 50, 1000))])
+    assert ps.last_dispatches(trace, "k_a", 2) == [5.0, 7.0]
