@@ -20,9 +20,13 @@ SwiGLU epilogue (two thirds of the layer's flops), timed on its own through the 
 entry point with w2 = y = NULL.  Its bound is chosen by arithmetic intensity: algorithmic
 flop per algorithmic byte (each active expert's W1 and W3 read once, xd read once, h
 written once) against the ridge point 2500 TFLOP/s / 8 TB/s; with skewed routing most
-experts see a few rows, so at X-MoE Large the kernel sits below the ridge (HBM-bound).  Its "traffic" (HBM bytes per launch from FETCH_SIZE and
-WRITE_SIZE counters, scaled by a plain copy's reading) comes from the committed counter
-summary and is reported only while the kernel sources still hash to what was profiled.
+experts see a few rows, so at X-MoE Large the kernel sits below the ridge (HBM-bound).
+Its "traffic" (bytes per launch between the L2 and the memory fabric, from FETCH_SIZE and
+WRITE_SIZE counters scaled by a plain copy's reading; Infinity Cache hits included) comes
+from the committed counter summary and is reported only while the kernel sources still
+hash to what was profiled.  Step times are the median of per-step event intervals.  The
+"parity" object compares the timed step's routing (every token) and output (the CPU
+baseline's sample) with the oracle.
 """
 from __future__ import annotations
 
@@ -41,7 +45,7 @@ HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, published
 UP_KERNEL = "expert_gemm_kernel<moe::bf16_t, 2, 1"   # name prefix in profiler output
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "xmoe_large_expert_up_traffic.md")
-COPY_BYTES = 1 << 30
+COPY_BYTES = 1 << 30      # counter calibration copy
 
 
 def log(msg):
@@ -124,18 +128,32 @@ def algorithmic(cfg, counts):
 
 
 def time_calls(fn, iters, stream):
+    """Median ms per call over `iters` back-to-back calls, each bracketed by its own pair of
+    events on `stream` (an interval also holds the launch gaps inside the call)."""
+    return time_steps(fn, iters, stream)["median"]
+
+
+def time_steps(fn, iters, stream):
+    """Per-call ms of `iters` back-to-back calls: dict(median, mean, min, max, all)."""
+    import statistics
+
     import torch
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(iters):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    ev[0].record(stream)
+    for i in range(iters):
         fn()
-    end.record(stream)
-    end.synchronize()
-    return start.elapsed_time(end) / iters        # ms per call
+        ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]
+    return {"median": statistics.median(ms), "mean": sum(ms) / len(ms), "min": min(ms),
+            "max": max(ms), "all": ms}
 
 
-def cpu_baseline(cfg, d, seed, target_s):
-    """The oracle, as it is, on the first tokens of the same workload (bounded sample)."""
+def cpu_baseline(cfg, d, seed, target_s, gpu_out, gpu_te, gpu_tw, refined):
+    """The oracle, as it is, on the first tokens of the same workload (bounded sample).
+    Returns (cpu_baseline record, parity record): the sample's oracle output is compared
+    with the GPU's output for the same tokens, and the oracle's routing of every token of
+    the batch with the GPU's."""
     import numpy as np
 
     import oracle
@@ -155,23 +173,48 @@ def cpu_baseline(cfg, d, seed, target_s):
                 w_host[n][e] = W.to_host(d[n][e], dt)
             loaded.add(e)
         t0 = time.perf_counter()
-        _, secs = oracle.layer_forward(dt, x_all[:ntok], wg, bias, w_host["w1"], w_host["w3"],
-                                       w_host["w2"], cfg.k, stage_seconds=True)
-        return time.perf_counter() - t0, secs
+        out, secs = oracle.layer_forward(dt, x_all[:ntok], wg, bias, w_host["w1"], w_host["w3"],
+                                         w_host["w2"], cfg.k, stage_seconds=True)
+        return time.perf_counter() - t0, secs, out
 
     # The oracle parallelises over the rows of each expert, so tokens/s grows with the
     # sample; grow it until one run takes about target_s (or the whole batch is used).
     ntok = 16
     while True:
-        wall, secs = run(ntok)
+        wall, secs, out_ref = run(ntok)
         if wall >= 0.7 * target_s or ntok >= cfg.T:
             break
         ntok = int(min(cfg.T, ntok * min(8.0, max(2.0, target_s / max(wall, 1e-3)))))
-    return {"value": ntok / wall, "unit": "tokens/s", "cores": oracle.num_threads(),
+    base = {"value": ntok / wall, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"first {ntok} of {cfg.T} tokens of the same {cfg.name} layer (same weights), "
                       f"oracle_layer_forward end to end, {wall:.1f} s; stage seconds gate/buffers/"
                       f"dispatch/experts/combine = {', '.join(f'{s:.2f}' for s in secs)}"}
+    # parity: routing of the whole batch (oracle gate on every token), output of the sample
+    te_ref, tw_ref, _, l64 = oracle.gate_topk(dt, x_all, wg, bias, cfg.k, want_logits=True)
+    m = min(cfg.k + 1, cfg.E)
+    top = -np.sort(-l64, axis=1)[:, :m]
+    gaps = ((top[:, :-1] - top[:, 1:]) / np.maximum(1.0, np.abs(top[:, :-1]))).min(axis=1) \
+        if m > 1 else np.full(cfg.T, np.inf)
+    g = W.bf16_bits_to_f32(gpu_out[:ntok]) if dt == "bf16" else gpu_out[:ntok]
+    r = W.bf16_bits_to_f32(out_ref) if dt == "bf16" else out_ref
+    g, r = g.astype(np.float64), r.astype(np.float64)
+    scale = float(np.max(np.abs(r))) or 1.0
+    parity = {
+        "routing_tokens": cfg.T,
+        "routing_mismatches": int(np.any(gpu_te != te_ref, axis=1).sum()),
+        "near_tie_tokens": int((gaps <= 1e-6).sum()),
+        "band_tokens_1e-6_1e-5": int(((gaps > 1e-6) & (gaps <= 1e-5)).sum()),
+        "tokens_decided_from_exact_logits": refined,
+        "top_weights_max_abs_err": float(np.max(np.abs(gpu_tw - tw_ref))),
+        "out_tokens_compared": ntok,
+        "out_max_abs_rel": float(np.max(np.abs(g - r))) / scale,
+        "out_rms_rel": float(np.sqrt(np.mean((g - r) ** 2)) / (np.sqrt(np.mean(r * r)) or 1.0)),
+        "tolerance": 1e-4 if dt == "f32" else 2e-2,
+        "note": "oracle gate on every token of the batch; oracle layer output on the "
+                "cpu_baseline sample, against the GPU output of the timed step",
+    }
+    return base, parity
 
 
 def weight_stream(cfg, args, dev):
@@ -259,9 +302,15 @@ def main():
     log(f"bench: routing {W.routing_summary(counts)}; timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms_events = time_calls(step, args.steps, stream)
+    steps_ms = time_steps(step, args.steps, stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_events = steps_ms["median"]
+    # what the timed step produced, for the parity record
+    out_host = W.to_host(out, cfg.dtype)
+    te_host = W.to_host(bufs_f["top_experts"], None)
+    tw_host = W.to_host(bufs_f["top_weights"], None)
+    refined = int(W.to_host(ws[4:8].view(torch.int32), None)[0])
 
     step_staged()
     torch.cuda.synchronize()
@@ -315,15 +364,6 @@ def main():
         roof = {"bound": "hbm", "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(up_gbs / HBM_PEAK_GBS, 4)}
     stage_report = {n: round(v * 1e3, 2) for n, v in st_ms.items()}
-    # plain device-to-device copy of 512 MiB in the same run: the practical ceiling for
-    # the row-moving stages (read + write bytes)
-    cp_src = torch.empty(COPY_BYTES // 2, dtype=torch.uint8, device=dev)
-    cp_dst = torch.empty_like(cp_src)
-    cp_dst.copy_(cp_src)
-    torch.cuda.synchronize()
-    copy_ms = time_calls(lambda: cp_dst.copy_(cp_src), 10, stream)
-    copy_gbs = 2.0 * cp_src.numel() / (copy_ms * 1e-3) / 1e9
-    del cp_src, cp_dst
     # launch floor for the buffer build (three kernels: histogram, scan, scatter): the same
     # number of one-element fill kernels back to back on the same stream, timed the same way
     tiny = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -336,7 +376,6 @@ def main():
     torch.cuda.synchronize()
     floor_us = time_calls(chain3, args.steps, stream) * 1e3
     bw = {
-        "copy_GBs": copy_gbs,
         "dispatch_GBs": alg["dispatch_bytes"] / (st_ms["dispatch"] * 1e-3) / 1e9,
         "combine_GBs": alg["combine_bytes"] / (st_ms["combine"] * 1e-3) / 1e9,
         "grouped_gemm_GBs": alg["gemm_bytes"] / (g_ms * 1e-3) / 1e9,
@@ -392,7 +431,9 @@ def main():
         "metric": METRIC if cfg.name == "xmoe_large" else METRIC.replace("X-MoE Large", cfg.name),
         "value": cfg.T / (ms_events * 1e-3), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_events, "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": ms_events,
+        "step_ms": {k_: round(steps_ms[k_], 4) for k_ in ("median", "mean", "min", "max")},
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "F": cfg.F,
                    "k": cfg.k, "gate_bias": None if cfg.bias is None else f"{cfg.bias[0]}({cfg.bias[1]})",
@@ -401,6 +442,10 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof | {
             "traffic": recorded_traffic(cfg.name),
+            "traffic_note": "bytes per launch the L2 exchanged with the memory fabric (FETCH_SIZE "
+                            "+ WRITE_SIZE, scaled by a plain copy's reading): Infinity Cache hits "
+                            "included, so an upper bound on HBM bytes; null once the kernel "
+                            "sources differ from the profiled ones",
             "kernel": "expert_gemm_kernel, gate/up product + SwiGLU, dispatch fused (as in the timed step)",
             "per_launch": {"flop": alg["up_flops"], "bytes": alg["up_bytes"],
                            "us": round(up_ms * 1e3, 1), "flop_per_byte": round(intensity, 1),
@@ -423,8 +468,6 @@ def main():
         "bandwidth": {k_: round(v, 1) for k_, v in bw.items()}
         | {"dispatch_frac_hbm": round(bw["dispatch_GBs"] / HBM_PEAK_GBS, 4),
            "combine_frac_hbm": round(bw["combine_GBs"] / HBM_PEAK_GBS, 4),
-           "dispatch_frac_copy": round(bw["dispatch_GBs"] / bw["copy_GBs"], 4),
-           "combine_frac_copy": round(bw["combine_GBs"] / bw["copy_GBs"], 4),
            "grouped_gemm_frac_hbm": round(bw["grouped_gemm_GBs"] / HBM_PEAK_GBS, 4)},
         "wall_ms_per_step": wall_ms,
     }
@@ -432,7 +475,8 @@ def main():
         rec["backward"] = bwd
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
-        rec["cpu_baseline"] = cpu_baseline(cfg, d, args.seed, args.cpu_seconds)
+        rec["cpu_baseline"], rec["parity"] = cpu_baseline(cfg, d, args.seed, args.cpu_seconds,
+                                                          out_host, te_host, tw_host, refined)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -51,8 +51,11 @@ moe_status_t launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
         if (st_ != MOE_OK) return st_;       \
     } while (0)
 
+// Gate workspace: a 256-byte header (int32 1: tokens decided from exact logits), then the
+// fp32 partial logits [split][T][E].
+constexpr size_t kGateHeader = 256;
 size_t gate_ws(int dt, int T, int H, int E) {
-    return round_up((size_t)moe::gate_splits(dt, T, H, E) * T * E * sizeof(float));
+    return kGateHeader + round_up((size_t)moe::gate_splits(dt, T, H, E) * T * E * sizeof(float));
 }
 size_t pft_ws(int T, int k, int E) { return round_up(moe::pft_ws_bytes((long long)T * k, E)); }
 size_t gemm_ws(long long N, int E) { return round_up(moe::gemm_ws_bytes(N, E)); }
@@ -99,10 +102,13 @@ MOE_API moe_status_t moe_gate_topk(moe_dtype_t dt, int T, int H, int E, int k,
     MOE_TRY(check_ptrs({x, wg, top_experts, top_weights, ws}));
     if (bias && !aligned16(bias)) return MOE_ERR_MISALIGNED;
     if (ws_bytes < gate_ws(dt, T, H, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-    float* partials = static_cast<float*>(ws);
-    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, as_stream(stream))));
-    return launched(moe::launch_topk(T, E, k, routing, moe::gate_splits(dt, T, H, E), partials,
-                                     bias, top_experts, top_weights, as_stream(stream)));
+    int* refined = static_cast<int*>(ws) + 1;
+    float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + kGateHeader);
+    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, refined,
+                                             as_stream(stream))));
+    return launched(moe::launch_topk(dt, T, E, k, routing, moe::gate_splits(dt, T, H, E),
+                                     partials, bias, x, wg, H, top_experts, top_weights, refined,
+                                     as_stream(stream)));
 }
 
 MOE_API moe_status_t moe_pft_build(int T, int k, int E, const int32_t* top_experts,
@@ -189,12 +195,14 @@ MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int 
     if (ws_bytes < need_pft + need_gate + gemm_ws(N, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     char* w = static_cast<char*>(ws);
     void* ws_pft = w;                       // error word stays at byte 0
-    float* partials = reinterpret_cast<float*>(w + need_pft);
+    int* refined = reinterpret_cast<int*>(w) + 1;   // beside the error word
+    float* partials = reinterpret_cast<float*>(w + need_pft + kGateHeader);
     void* ws_gemm = w + need_pft + need_gate;
     const hipStream_t s = as_stream(stream);
-    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, s)));
-    MOE_TRY(launched(moe::launch_topk(T, E, k, routing, moe::gate_splits(dt, T, H, E), partials,
-                                      bias, b->top_experts, b->top_weights, s)));
+    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, refined, s)));
+    MOE_TRY(launched(moe::launch_topk(dt, T, E, k, routing, moe::gate_splits(dt, T, H, E),
+                                      partials, bias, x, wg, H, b->top_experts, b->top_weights,
+                                      refined, s)));
     MOE_TRY(launched(moe::launch_pft(T, k, E, b->top_experts, b->counts, b->offsets, b->token_ids,
                                      b->expert_ids, b->dest_pos, ws_pft, s)));
     if (b->xd) {

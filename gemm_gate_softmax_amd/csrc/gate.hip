@@ -7,6 +7,12 @@
 // logit.  Softmax weights are softmax over all E logits renormalised over the k picks,
 // which equals exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0) because the full denominator
 // cancels; sigmoid weights are s_j / sum_{i<k} s_i with s = 1 / (1 + exp(-l)).
+//
+// The logits come from the MFMA GEMM as fp32 sums, which differ from the exact sums by
+// accumulation rounding (a few 1e-6 at H = 7168).  The layer's logit is the exact sum
+// rounded once to fp32, so near ties are re-decided: the logits involved are recomputed
+// as double sums (exact products, double accumulation) and rounded once, and the picks
+// and their order are those of these values.
 #include "device.h"
 #include "launch.h"
 
@@ -26,20 +32,111 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
+// The fp32 logits the layer defines for token t and experts e1, e2: the H products summed
+// in double (each product of two fp32 or bf16 values is exact in double), the bias added
+// in double, then one rounding to fp32.  One wave; every lane returns the same values (the
+// butterfly adds commute).  Each lane issues the loads of kRefChunks 16-byte chunks of the
+// three rows before it uses any, so a pass costs about one memory latency.
+constexpr int kRefChunks = 4;
+
+template <typename T>
+__device__ void exact_logits2(const T* __restrict__ x, const T* __restrict__ wg,
+                              const float* __restrict__ bias, int H, int t, int e1, int e2,
+                              int lane, float* v1, float* v2) {
+    constexpr int P = 16 / (int)sizeof(T);
+    const int chunks = H / P;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * H);
+    const uint4* w1 = reinterpret_cast<const uint4*>(wg + (size_t)e1 * H);
+    const uint4* w2 = reinterpret_cast<const uint4*>(wg + (size_t)e2 * H);
+    double s1 = 0.0, s2 = 0.0;
+    for (int c0 = lane; c0 < chunks; c0 += kRefChunks * kWave) {
+        uint4 xa[kRefChunks], wa[kRefChunks], wb[kRefChunks];
+#pragma unroll
+        for (int u = 0; u < kRefChunks; ++u) {
+            const int c = c0 + u * kWave;
+            const bool in = c < chunks;
+            xa[u] = in ? xr[c] : make_uint4(0, 0, 0, 0);
+            wa[u] = in ? w1[c] : make_uint4(0, 0, 0, 0);
+            wb[u] = in ? w2[c] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kRefChunks; ++u) {
+            float a[P], b[P], d[P];
+            unpack16(xa[u], a, T{});
+            unpack16(wa[u], b, T{});
+            unpack16(wb[u], d, T{});
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                const double xv = static_cast<double>(a[i]);
+                s1 = fma(xv, static_cast<double>(b[i]), s1);
+                s2 = fma(xv, static_cast<double>(d[i]), s2);
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        s1 += __shfl_xor(s1, m, kWave);
+        s2 += __shfl_xor(s2, m, kWave);
+    }
+    if (bias) {
+        s1 += static_cast<double>(bias[e1]);
+        s2 += static_cast<double>(bias[e2]);
+    }
+    *v1 = static_cast<float>(s1);
+    *v2 = static_cast<float>(s2);
+}
+
+// n rounds of wave max over the keys (consumed): lane j < n returns pick j; *last is the
+// n-th pick on every lane.
+template <int NPER>
+__device__ __forceinline__ uint64_t select_top(uint64_t (&key)[NPER], int n, int lane,
+                                               uint64_t* last) {
+    uint64_t mine = 0, w = 0;
+    for (int j = 0; j < n; ++j) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < NPER; ++i) best = key[i] > best ? key[i] : best;
+        w = wave_max_u64(best);
+        if (lane == j) mine = w;
+        const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(w));
+        if (lane == (e & 63)) {
+#pragma unroll
+            for (int i = 0; i < NPER; ++i)
+                if (i == (e >> 6)) key[i] = 0ull;
+        }
+    }
+    *last = w;
+    return mine;
+}
+
+// Relative gap below which two fp32-accumulated logits are re-decided from exact sums:
+// 2^-13 (1.2e-4), about fifty times the largest difference between fp32-accumulated and
+// double logits measured on these shapes (2.5e-6), so every other order is already the
+// order of the exact values.
+#ifndef MOE_TIE_REL
+#define MOE_TIE_REL (1.0f / 8192.0f)
+#endif
+constexpr float kTieRel = MOE_TIE_REL;
+
 // logit(t, e) = (partials[0][t][e] + partials[1][t][e] + ...) + bias[e], summed in split
-// order so the result does not depend on scheduling.
-template <int NPER, int ROUTE>
-__global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(const float* __restrict__ partials,
-                                                                      const float* __restrict__ bias,
-                                                                      int T, int E, int k, int splits,
-                                                                      int32_t* __restrict__ top_experts,
-                                                                      float* __restrict__ top_weights) {
+// order so the result does not depend on scheduling.  Near ties are re-decided exactly:
+// among a token's picks and the first expert left out, any two neighbours closer than
+// kTieRel (relative, at least absolute) get their logits recomputed with exact_logit, and
+// when the last pick and the first one left out are that close, so does every expert
+// within kTieRel of the last pick.  Every other pair is farther apart than twice the
+// fp32 accumulation error, so the final order is that of the exactly rounded logits.
+// Such tokens are counted in *refined.
+template <typename T, int NPER, int ROUTE>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(
+    const float* __restrict__ partials, const float* __restrict__ bias, int T_, int E, int k,
+    int splits, const T* __restrict__ x, const T* __restrict__ wg, int H,
+    int32_t* __restrict__ top_experts, float* __restrict__ top_weights, int* refined) {
     const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (t >= T) return;
+    if (t >= T_) return;
     const int lane = threadIdx.x & 63;
-    const size_t stride = (size_t)T * E;
+    const size_t stride = (size_t)T_ * E;
     const float* row = partials + (size_t)t * E;
-    uint64_t key[NPER];
+    uint64_t key[NPER], orig[NPER];
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
         const int e = lane + kWave * i;
@@ -51,25 +148,80 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(const floa
         } else {
             key[i] = 0ull;
         }
+        orig[i] = key[i];
     }
-    uint64_t mine = 0;  // lane j keeps pick j
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < NPER; ++i) best = key[i] > best ? key[i] : best;
-        const uint64_t w = wave_max_u64(best);
-        if (lane == j) mine = w;
-        const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(w));
-        if (lane == (e & 63)) {
-#pragma unroll
-            for (int i = 0; i < NPER; ++i)
-                if (i == (e >> 6)) key[i] = 0ull;
-        }
-    }
+    // the picks and, when there is one, the first expert left out (the (k+1)-th)
+    const bool more = k < E;
+    uint64_t last;
+    uint64_t mine = select_top(key, more ? k + 1 : k, lane, &last);
+    // adjacent gaps among them: lane j < k compares pick j with the next one
     const float lj = key_logit(mine);
-    const float l0 = __shfl(lj, 0, kWave);
+    const float lup = __shfl(lj, lane + 1 < kWave ? lane + 1 : lane, kWave);
+    const float lnext = lane + 1 < k ? lup : key_logit(last);
+    const bool close = (lane + 1 < k || (lane + 1 == k && more)) &&
+                       (lj - lnext) <= kTieRel * fmaxf(1.0f, fabsf(lj));
+    const uint64_t closes = __ballot(close);          // bit j: picks j and j + 1 are close
+    if (closes != 0ull) {
+        // Candidates, refined two at a time (pend: a candidate waiting for a partner):
+        // when the last pick and the first one left out are close, every expert left out
+        // that lies within kTieRel of the last pick; then every pick in a close pair.
+        // (the expert ids are wave-uniform values held in locals, so no cross-lane read
+        // happens inside the one-lane branches below)
+#define MOE_REFINE_PAIR(EA, EB)                                                               \
+        do {                                                                                 \
+            const int ea_ = (EA), eb_ = (EB);                                                \
+            float va_, vb_;                                                                  \
+            exact_logits2(x, wg, bias, H, t, ea_, eb_, lane, &va_, &vb_);                    \
+            _Pragma("unroll") for (int i_ = 0; i_ < NPER; ++i_) {                            \
+                if (lane == (ea_ & 63) && i_ == (ea_ >> 6)) orig[i_] = make_key(va_, ea_);   \
+                if (lane == (eb_ & 63) && i_ == (eb_ >> 6)) orig[i_] = make_key(vb_, eb_);   \
+            }                                                                                \
+        } while (0)
+#define MOE_TAKE(EE)                                                                          \
+        do {                                                                                 \
+            const int ee_ = (EE);                                                            \
+            if (pend < 0) pend = ee_;                                                        \
+            else { MOE_REFINE_PAIR(pend, ee_); pend = -1; }                                  \
+        } while (0)
+        int pend = -1;
+        if ((closes >> (k - 1)) & 1ull) {
+            const float lk = __shfl(lj, k - 1, kWave);
+            const float floor_l = lk - kTieRel * fmaxf(1.0f, fabsf(lk));
+#pragma unroll
+            for (int i = 0; i < NPER; ++i) {
+                const int e = lane + kWave * i;
+                uint64_t cand = __ballot(e < E && orig[i] < last && key_logit(orig[i]) >= floor_l);
+                while (cand) {
+                    const int l = __ffsll(static_cast<long long>(cand)) - 1;
+                    cand &= cand - 1;
+                    MOE_TAKE(l + kWave * i);
+                }
+            }
+        }
+        const int npick = more ? k + 1 : k;
+        uint64_t need = (closes | (closes << 1)) & (npick < 64 ? ((1ull << npick) - 1) : ~0ull);
+        if (npick > 64 && ((closes >> 63) & 1ull)) {
+            // the first expert left out of 64 picks sits beyond the lanes: take it here
+            MOE_TAKE(static_cast<int>(0xffffffffu - static_cast<uint32_t>(last)));
+        }
+        const int pe = static_cast<int>(0xffffffffu - static_cast<uint32_t>(mine));
+        while (need) {
+            const int j = __ffsll(static_cast<long long>(need)) - 1;
+            need &= need - 1;
+            MOE_TAKE(__shfl(pe, j, kWave));
+        }
+        if (pend >= 0) MOE_REFINE_PAIR(pend, pend);
+#undef MOE_TAKE
+#undef MOE_REFINE_PAIR
+        if (lane == 0 && refined) atomicAdd(refined, 1);
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) key[i] = orig[i];
+        mine = select_top(key, k, lane, &last);
+    }
+    const float lp = key_logit(mine);
+    const float l0 = __shfl(lp, 0, kWave);
     float ex = 0.0f;
-    if (lane < k) ex = ROUTE == 0 ? expf(lj - l0) : 1.0f / (1.0f + expf(-lj));
+    if (lane < k) ex = ROUTE == 0 ? expf(lp - l0) : 1.0f / (1.0f + expf(-lp));
     const float z = wave_sum_f32(ex);
     if (lane < k) {
         top_experts[(size_t)t * k + lane] = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(mine));
@@ -77,29 +229,43 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(const floa
     }
 }
 
-template <int NPER>
-hipError_t launch_topk_n(int T, int E, int k, int routing, int splits, const float* partials,
-                         const float* bias, int32_t* te, float* tw, hipStream_t s) {
-    const int blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+template <typename T, int NPER>
+hipError_t launch_topk_n(int T_, int E, int k, int routing, int splits, const float* partials,
+                         const float* bias, const void* x, const void* wg, int H, int32_t* te,
+                         float* tw, int* refined, hipStream_t s) {
+    const int blocks = (T_ + kWavesPerBlock - 1) / kWavesPerBlock;
+    const T* xt = static_cast<const T*>(x);
+    const T* wt = static_cast<const T*>(wg);
     if (routing == 0)
-        hipLaunchKernelGGL((topk_kernel<NPER, 0>), dim3(blocks), dim3(kWave * kWavesPerBlock), 0, s,
-                           partials, bias, T, E, k, splits, te, tw);
+        hipLaunchKernelGGL((topk_kernel<T, NPER, 0>), dim3(blocks), dim3(kWave * kWavesPerBlock), 0, s,
+                           partials, bias, T_, E, k, splits, xt, wt, H, te, tw, refined);
     else
-        hipLaunchKernelGGL((topk_kernel<NPER, 1>), dim3(blocks), dim3(kWave * kWavesPerBlock), 0, s,
-                           partials, bias, T, E, k, splits, te, tw);
+        hipLaunchKernelGGL((topk_kernel<T, NPER, 1>), dim3(blocks), dim3(kWave * kWavesPerBlock), 0, s,
+                           partials, bias, T_, E, k, splits, xt, wt, H, te, tw, refined);
     return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_topk_t(int T_, int E, int k, int routing, int splits, const float* partials,
+                         const float* bias, const void* x, const void* wg, int H, int32_t* te,
+                         float* tw, int* refined, hipStream_t s) {
+#define MOE_TOPK(NPER) launch_topk_n<T, NPER>(T_, E, k, routing, splits, partials, bias, x, wg, H, te, tw, refined, s)
+    if (E <= 64) return MOE_TOPK(1);
+    if (E <= 128) return MOE_TOPK(2);
+    if (E <= 256) return MOE_TOPK(4);
+    if (E <= 512) return MOE_TOPK(8);
+    return MOE_TOPK(16);
+#undef MOE_TOPK
 }
 
 }  // namespace
 
-hipError_t launch_topk(int T, int E, int k, int routing, int splits, const float* partials,
-                       const float* bias, int32_t* te, float* tw, hipStream_t s) {
+hipError_t launch_topk(int dt, int T, int E, int k, int routing, int splits, const float* partials,
+                       const float* bias, const void* x, const void* wg, int H, int32_t* te,
+                       float* tw, int* refined, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    if (E <= 64) return launch_topk_n<1>(T, E, k, routing, splits, partials, bias, te, tw, s);
-    if (E <= 128) return launch_topk_n<2>(T, E, k, routing, splits, partials, bias, te, tw, s);
-    if (E <= 256) return launch_topk_n<4>(T, E, k, routing, splits, partials, bias, te, tw, s);
-    if (E <= 512) return launch_topk_n<8>(T, E, k, routing, splits, partials, bias, te, tw, s);
-    return launch_topk_n<16>(T, E, k, routing, splits, partials, bias, te, tw, s);
+    return dt == 0 ? launch_topk_t<float>(T, E, k, routing, splits, partials, bias, x, wg, H, te, tw, refined, s)
+                   : launch_topk_t<bf16_t>(T, E, k, routing, splits, partials, bias, x, wg, H, te, tw, refined, s);
 }
 
 }  // namespace moe

@@ -122,6 +122,7 @@ struct GemmParams {
     void* out3;             // kEpiSwiGLUPair: g
     int k_slices;           // dense product: k-slices per K split
     int group_tok;          // expert product: token tiles per L2-sharing block (0: kGroupTok)
+    int* zero_word;         // dense product: set to 0 by workgroup 0 (nullable)
 };
 
 // Writes 4 consecutive fp32 partial logits of one token (per-element bounds: E need not be
@@ -522,6 +523,7 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
 __global__ __launch_bounds__(kThreads, 1) void dense_gemm_kernel(GemmParams<T, NB> p) {
     __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, NB, S, RB>::kLdsBytes];
+    if (blockIdx.x == 0 && threadIdx.x == 0 && p.zero_word) *p.zero_word = 0;
     // work item L = (split, token tile, feature tile), feature tile fastest so the
     // workgroups an XCD runs at once share their activation rows through its L2
     const int ntt = (p.dense_rows + BT - 1) / BT;
@@ -683,8 +685,9 @@ __host__ __device__ inline int gate_k_slices(int dt, int T, int H, int E) {
 
 template <typename T>
 hipError_t gate_logits_t(int dt, int T_, int H, int E, const void* x, const void* wg,
-                         float* partials, hipStream_t s) {
+                         float* partials, int* zero_word, hipStream_t s) {
     GemmParams<T, 1> p{};
+    p.zero_word = zero_word;
     p.act = static_cast<const T*>(x);
     p.act_rows = T_;
     p.K = H;
@@ -925,10 +928,10 @@ int gate_splits(int dt, int T, int H, int E) {
 }
 
 hipError_t launch_gate_logits(int dt, int T, int H, int E, const void* x, const void* wg,
-                              float* partials, hipStream_t s) {
+                              float* partials, int* zero_word, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    return dt == 0 ? gate_logits_t<float>(dt, T, H, E, x, wg, partials, s)
-                   : gate_logits_t<bf16_t>(dt, T, H, E, x, wg, partials, s);
+    return dt == 0 ? gate_logits_t<float>(dt, T, H, E, x, wg, partials, zero_word, s)
+                   : gate_logits_t<bf16_t>(dt, T, H, E, x, wg, partials, zero_word, s);
 }
 
 hipError_t launch_grouped_gemm(int dt, int N, int E, int H, int F, const void* xd,

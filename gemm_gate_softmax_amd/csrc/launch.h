@@ -10,14 +10,17 @@
 namespace moe {
 
 // Gate logits x.Wg^T as gate_splits() fp32 partial sums over K splits, [split][T][E] in
-// `partials` (no bias).
+// `partials` (no bias).  *zero_word (may be NULL) is set to 0 by the launch.
 int gate_splits(int dt, int T, int H, int E);
 hipError_t launch_gate_logits(int dt, int T, int H, int E, const void* x, const void* wg,
-                              float* partials, hipStream_t s);
+                              float* partials, int* zero_word, hipStream_t s);
 // Top-k selection and renormalised weights (routing 0 softmax, 1 sigmoid) from logits =
-// (sum of the partials in split order) + bias.
-hipError_t launch_topk(int T, int E, int k, int routing, int splits, const float* partials,
-                       const float* bias, int32_t* top_experts, float* top_weights, hipStream_t s);
+// (sum of the partials in split order) + bias; near-tie tokens are re-decided from exact
+// logits recomputed from x and wg, and counted in *refined (may be NULL).
+hipError_t launch_topk(int dt, int T, int E, int k, int routing, int splits,
+                       const float* partials, const float* bias, const void* x, const void* wg,
+                       int H, int32_t* top_experts, float* top_weights, int* refined,
+                       hipStream_t s);
 
 size_t pft_ws_bytes(long long N, int E);
 hipError_t launch_pft(int T, int k, int E, const int32_t* top_experts, int32_t* counts,

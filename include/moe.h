@@ -84,6 +84,10 @@ const char *moe_status_string(moe_status_t status);
  * Top-k softmax gate (X-MoE review, 训练流程 step 2: gating produced straight in buffer
  * form, no dense dispatch mask; FSMoE report, 第三部分 item 1, Gating Function module).
  *   logit[t][e]        = sum_h x[t][h] * wg[e][h] + bias[e]          (fp32 accumulate)
+ *   The selection is that of the exactly rounded logits fp32(exact sum + bias): a token
+ *   whose k + 1 largest fp32-accumulated logits hold two neighbours within 2^-13
+ *   (relative, at least absolute) of each other has the logits involved recomputed as
+ *   double sums and rounded once, and is decided from those.
  *   top_experts[t][j]  = the j-th expert in the order (logit desc, expert id asc), j < k
  *   top_weights[t][j]  = MOE_ROUTE_SOFTMAX: softmax(logit[t])[pick j] renormalised over
  *                        the k picks = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)
@@ -93,7 +97,8 @@ const char *moe_status_string(moe_status_t status);
  * bias may be NULL (no bias).  Outputs: top_experts [T][k] int32, top_weights [T][k] fp32.
  * ws: moe_workspace_bytes(MOE_WS_GATE, ...) bytes (depends on T, H, E and dt: it holds
  * fp32 partial logits over up to 8 splits of the hidden dimension, which the top-k step
- * adds in split order before the bias).
+ * adds in split order before the bias).  After the call completes, the int32 at byte 4 of
+ * ws holds the number of tokens decided from recomputed exact logits.
  */
 moe_status_t moe_gate_topk(moe_dtype_t dt, int T, int H, int E, int k, moe_routing_t routing,
                            const void *x, const void *wg, const float *bias,
@@ -185,8 +190,10 @@ typedef struct moe_layer_bufs {
  * host synchronisation.  x [T][H] -> out [T][H]; intermediates land in *bufs (every
  * pointer required except xd).  bufs->xd NULL fuses the dispatch into the expert product
  * (rows gathered from x through token_ids as they are loaded, the next step the X-MoE
- * review's padding-free dispatch allows): xd is not written and the results are identical.  ws: moe_workspace_bytes(MOE_WS_LAYER, ...) bytes; its byte-0 int32
- * is the error word of moe_pft_build.
+ * review's padding-free dispatch allows): xd is not written and the results are identical.
+ * ws: moe_workspace_bytes(MOE_WS_LAYER, ...) bytes; after the call its byte-0 int32 is the
+ * error word of moe_pft_build and its byte-4 int32 the gate's count of tokens decided from
+ * exact logits (moe_gate_topk).
  */
 moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k,
                                moe_routing_t routing, const void *x, const void *wg,

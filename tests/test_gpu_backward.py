@@ -152,11 +152,14 @@ def _sub_offsets(experts_of_rows):
     return uniq, np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["xmoe_small", "xmoe_large"])
 def test_backward_full_size_sampled(name):
     """At the benchmark shapes, on the launch the benchmark times: dtw and dx of sampled
-    tokens, all weight gradients of one small expert, dWg and dbias of that expert, and the
-    zero sum of dbias, each against the oracle's stage functions on just the rows involved."""
+    tokens, all weight gradients of the expert with the fewest rows (outer-product route)
+    and of the expert with the most rows (tile-GEMM route, K ranges of thousands of rows),
+    dWg and dbias of the first, and the zero sum of dbias, each against the oracle's stage
+    functions on just the rows involved."""
     cfg = W.CONFIGS[name]
     d, dout_h, bufs, grads = _run(cfg, "softmax", fuse=True)
     dt, k = cfg.dtype, cfg.k
@@ -203,18 +206,27 @@ def test_backward_full_size_sampled(name):
     gb = oracle.gate_backward(dt, x_h[ts], wg_h, bias_h, te[ts], dtw_ref, dx=dx_ref)
     check(as_f64(W.to_host(grads["dx"], dt)[ts], dt), gb["dx"], "dx (sampled tokens)")
 
-    # 2. every weight gradient of one small expert (the fewest rows), from all of its rows
+    # 2. every weight gradient of the expert with the fewest rows and of the one with the
+    # most, each from all of its rows
     active = np.where(counts > 0)[0]
+    slot = {}
+    for t_ in range(cfg.T):
+        for j_ in range(k):
+            slot[int(dp[t_, j_])] = (t_, j_)
+    for e in (int(active[np.argmin(counts[active])]), int(active[np.argmax(counts[active])])):
+        prow = np.arange(off[e], off[e + 1])
+        tj = [slot[int(p)] for p in prow]
+        assert all(int(tok[p]) == t for p, (t, _) in zip(prow, tj))
+        dy_e = np.stack([tw[t, j] * as_f64(dout_h[t], dt) for t, j in tj])
+        w1s, w3s, w2s = expert_w([e])
+        h_e = W.to_host(bufs["h"][int(off[e]):int(off[e + 1])], dt)
+        eb = oracle.expert_backward(dt, x_h[[t for t, _ in tj]],
+                                    np.array([0, len(prow)], np.int32), w1s, w3s, w2s, dy_e, h=h_e)
+        for n in ("dw1", "dw3", "dw2"):
+            check(as_f64(W.to_host(grads[n][e], dt), dt), eb[n][0], f"{n}[{e}] ({len(prow)} rows)")
     e = int(active[np.argmin(counts[active])])
     prow = np.arange(off[e], off[e + 1])
-    tj = [(int(tok[p]), int(np.where(dp[tok[p]] == p)[0][0])) for p in prow]
-    dy_e = np.stack([tw[t, j] * as_f64(dout_h[t], dt) for t, j in tj])
-    w1s, w3s, w2s = expert_w([e])
-    h_e = W.to_host(bufs["h"][int(off[e]):int(off[e + 1])], dt)
-    eb = oracle.expert_backward(dt, x_h[[t for t, _ in tj]], np.array([0, len(prow)], np.int32),
-                                w1s, w3s, w2s, dy_e, h=h_e)
-    for n in ("dw1", "dw3", "dw2"):
-        check(as_f64(W.to_host(grads[n][e], dt), dt), eb[n][0], f"{n}[{e}] ({len(prow)} rows)")
+    tj = [slot[int(p)] for p in prow]
 
     # 3. dWg and dbias of that expert, from every token that picked it
     tpick = np.array(sorted({t for t, _ in tj}))
