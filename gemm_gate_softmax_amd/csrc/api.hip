@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "launch.h"
@@ -59,6 +60,9 @@ size_t gate_ws(int dt, int T, int H, int E) {
 }
 size_t pft_ws(int T, int k, int E) { return round_up(moe::pft_ws_bytes((long long)T * k, E)); }
 size_t gemm_ws(long long N, int E) { return round_up(moe::gemm_ws_bytes(N, E)); }
+size_t layer_ws(int dt, int T, int H, int E, int k) {
+    return pft_ws(T, k, E) + gate_ws(dt, T, H, E) + gemm_ws((long long)T * k, E);
+}
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
@@ -71,7 +75,7 @@ MOE_API size_t moe_workspace_bytes(int kind, int T, int H, int E, int F, int k, 
         case MOE_WS_GATE: return gate_ws(dt, T, H, E);
         case MOE_WS_PFT: return pft_ws(T, k, E);
         case MOE_WS_GEMM: return gemm_ws((long long)T * k, E);
-        case MOE_WS_LAYER: return pft_ws(T, k, E) + gate_ws(dt, T, H, E) + gemm_ws((long long)T * k, E);
+        case MOE_WS_LAYER: return layer_ws(dt, T, H, E, k);
         case MOE_WS_BACKWARD:
             if (check_dim(F) != MOE_OK) return 0;
             return round_up(moe::backward_ws_bytes(dt, T, H, E, F, k));
@@ -87,6 +91,9 @@ MOE_API const char* moe_status_string(moe_status_t s) {
         case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED: device pointer not 16-byte aligned";
         case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
         case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: the HIP runtime refused a kernel launch";
+        case MOE_ERR_SCRATCH_TOO_SMALL:
+            return "MOE_ERR_SCRATCH_TOO_SMALL: the call needs more scratch than the library's "
+                   "static buffer holds (MOE_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown moe_status_t";
     }
 }
@@ -173,32 +180,40 @@ MOE_API moe_status_t moe_combine(moe_dtype_t dt, int T, int k, int H, const void
                                         as_stream(stream)));
 }
 
-MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k,
-                                       moe_routing_t routing, const void* x, const void* wg,
-                                       const float* bias, const void* w1, const void* w3,
-                                       const void* w2,
-                                       void* out, const moe_layer_bufs* b, void* ws,
-                                       size_t ws_bytes, void* stream) {
+namespace {
+
+// Validation shared by the two layer-forward entry points (everything but the workspace).
+moe_status_t check_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k,
+                                 moe_routing_t routing, const void* x, const void* wg,
+                                 const float* bias, const void* w1, const void* w3,
+                                 const void* w2, void* out, const moe_layer_bufs* b) {
     if (!valid_dt(dt) || !valid_routing(routing) || !b) return MOE_ERR_INVALID_VALUE;
     MOE_TRY(check_route(T, E, k));
     MOE_TRY(check_dim(H));
     MOE_TRY(check_dim(F));
     if (T == 0) return MOE_OK;
-    MOE_TRY(check_ptrs({x, wg, w1, w3, w2, out, ws, b->top_experts, b->top_weights, b->counts,
+    MOE_TRY(check_ptrs({x, wg, w1, w3, w2, out, b->top_experts, b->top_weights, b->counts,
                         b->offsets, b->token_ids, b->expert_ids, b->dest_pos, b->h, b->y}));
     if (b->xd && !aligned16(b->xd)) return MOE_ERR_MISALIGNED;
     if ((b->a == nullptr) != (b->g == nullptr)) return MOE_ERR_INVALID_VALUE;
     if (b->a && (!aligned16(b->a) || !aligned16(b->g))) return MOE_ERR_MISALIGNED;
     if (bias && !aligned16(bias)) return MOE_ERR_MISALIGNED;
+    return MOE_OK;
+}
+
+// The stage chain on a validated call with T > 0 and a workspace of layer_ws() bytes.
+moe_status_t run_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k,
+                               moe_routing_t routing, const void* x, const void* wg,
+                               const float* bias, const void* w1, const void* w3,
+                               const void* w2, void* out, const moe_layer_bufs* b, void* ws,
+                               hipStream_t s) {
     const size_t need_pft = pft_ws(T, k, E), need_gate = gate_ws(dt, T, H, E);
     const long long N = (long long)T * k;
-    if (ws_bytes < need_pft + need_gate + gemm_ws(N, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     char* w = static_cast<char*>(ws);
     void* ws_pft = w;                       // error word stays at byte 0
     int* refined = reinterpret_cast<int*>(w) + 1;   // beside the error word
     float* partials = reinterpret_cast<float*>(w + need_pft + kGateHeader);
     void* ws_gemm = w + need_pft + need_gate;
-    const hipStream_t s = as_stream(stream);
     MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, refined, s)));
     MOE_TRY(launched(moe::launch_topk(dt, T, E, k, routing, moe::gate_splits(dt, T, H, E),
                                       partials, bias, x, wg, H, b->top_experts, b->top_weights,
@@ -215,6 +230,69 @@ MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int 
                                                          ws_gemm, s, b->a, b->g)));
     }
     return launched(moe::launch_combine(dt, T, k, H, b->y, b->dest_pos, b->top_weights, out, s));
+}
+
+}  // namespace
+
+MOE_API moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k,
+                                       moe_routing_t routing, const void* x, const void* wg,
+                                       const float* bias, const void* w1, const void* w3,
+                                       const void* w2,
+                                       void* out, const moe_layer_bufs* b, void* ws,
+                                       size_t ws_bytes, void* stream) {
+    MOE_TRY(check_layer_forward(dt, T, H, E, F, k, routing, x, wg, bias, w1, w3, w2, out, b));
+    if (T == 0) return MOE_OK;
+    MOE_TRY(check_ptrs({ws}));
+    if (ws_bytes < layer_ws(dt, T, H, E, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return run_layer_forward(dt, T, H, E, F, k, routing, x, wg, bias, w1, w3, w2, out, b, ws,
+                             as_stream(stream));
+}
+
+// ---- the layer forward without a caller workspace ----
+// Its scratch is one file-scope device array per GPU.  In host code `scratch` names a
+// host-side stand-in, not device memory: the array's device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that
+// address is ever handed to kernels.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the first call made
+// on that device, then cached).
+moe_status_t current_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_LAUNCH;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess || g_scratch[dev] == nullptr) return MOE_ERR_LAUNCH;
+    *out = g_scratch[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API moe_status_t moe_layer_forward_noalloc(moe_dtype_t dt, int T, int H, int E, int F,
+                                               int k, moe_routing_t routing, const void* x,
+                                               const void* wg, const float* bias,
+                                               const void* w1, const void* w3, const void* w2,
+                                               void* out, const moe_layer_bufs* b,
+                                               void* stream) {
+    MOE_TRY(check_layer_forward(dt, T, H, E, F, k, routing, x, wg, bias, w1, w3, w2, out, b));
+    if (T == 0) return MOE_OK;
+    if (layer_ws(dt, T, H, E, k) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH_TOO_SMALL;
+    void* ws = nullptr;
+    MOE_TRY(current_scratch(&ws));
+    return run_layer_forward(dt, T, H, E, F, k, routing, x, wg, bias, w1, w3, w2, out, b, ws,
+                             as_stream(stream));
 }
 
 MOE_API moe_status_t moe_layer_backward(moe_dtype_t dt, int T, int H, int E, int F, int k,

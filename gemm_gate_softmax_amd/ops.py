@@ -20,12 +20,14 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_F32, MOE_BF16 = 0, 1
 MOE_WS_GATE, MOE_WS_PFT, MOE_WS_GEMM, MOE_WS_LAYER, MOE_WS_BACKWARD = 0, 1, 2, 3, 4
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_VALUE", 2: "MOE_ERR_UNSUPPORTED",
-          3: "MOE_ERR_MISALIGNED", 4: "MOE_ERR_WORKSPACE_TOO_SMALL", 5: "MOE_ERR_LAUNCH"}
+          3: "MOE_ERR_MISALIGNED", 4: "MOE_ERR_WORKSPACE_TOO_SMALL", 5: "MOE_ERR_LAUNCH",
+          6: "MOE_ERR_SCRATCH_TOO_SMALL"}
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 ROUTING = {"softmax": 0, "sigmoid": 1}   # moe_routing_t
 EXPORTS = ("moe_workspace_bytes", "moe_status_string", "moe_gate_topk", "moe_pft_build",
            "moe_dispatch", "moe_grouped_gemm_swiglu", "moe_combine", "moe_layer_forward",
-           "moe_layer_backward")
+           "moe_layer_forward_noalloc", "moe_layer_backward")
 
 
 class MoeError(RuntimeError):
@@ -63,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_gemm_swiglu.argtypes = [i32] * 5 + [vp] * 2 + [i32] + [vp] * 7 + [sz, vp]
         L.moe_combine.argtypes = [i32] * 4 + [vp] * 5
         L.moe_layer_forward.argtypes = ([i32] * 7 + [vp] * 7 + [ctypes.POINTER(LayerBufs), vp, sz, vp])
+        L.moe_layer_forward_noalloc.argtypes = ([i32] * 7 + [vp] * 7 +
+                                                [ctypes.POINTER(LayerBufs), vp])
         L.moe_layer_backward.argtypes = ([i32] * 7 + [vp] * 6 + [ctypes.POINTER(LayerBufs)] +
                                          [vp] * 9 + [sz, vp])
         for f in EXPORTS[2:]:
@@ -283,6 +287,28 @@ def moe_layer_forward(x, wg, bias, w1, w3, w2, k, out=None, bufs=None, ws=None, 
         _ptr(w2), _ptr(out),
         ctypes.byref(cb), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out, bufs, ws
+
+
+def moe_layer_forward_noalloc(x, wg, bias, w1, w3, w2, k, out, bufs, stream=None,
+                              routing="softmax"):
+    """Whole layer on the library's static scratch (no workspace argument, nothing
+    allocated by the call).  out and bufs are required (as from alloc_layer_bufs).
+    Returns out."""
+    dt = dtype_code(x.dtype)
+    T, H = x.shape
+    E, F = w1.shape[0], w1.shape[1]
+    _need(x, "x"), _need(wg, "wg", x.dtype, (E, H))
+    _need(w1, "w1", x.dtype, (E, F, H)), _need(w3, "w3", x.dtype, (E, F, H))
+    _need(w2, "w2", x.dtype, (E, H, F))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,))
+    _need(out, "out", x.dtype, (T, H))
+    _need_ag(bufs, T * k, F, x.dtype)
+    cb = LayerBufs(*[_ptr(bufs.get(n)) for n, _ in LayerBufs._fields_])
+    _check("moe_layer_forward_noalloc", lib().moe_layer_forward_noalloc(
+        dt, T, H, E, F, k, ROUTING[routing], _ptr(x), _ptr(wg), _ptr(bias), _ptr(w1), _ptr(w3),
+        _ptr(w2), _ptr(out), ctypes.byref(cb), _stream(stream)))
+    return out
 
 
 def moe_layer_backward(x, wg, bias, w1, w3, w2, k, bufs, dout, grads=None, ws=None, stream=None,

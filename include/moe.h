@@ -50,7 +50,9 @@ typedef enum {
     MOE_ERR_UNSUPPORTED = 2,         /* a shape outside the limits above */
     MOE_ERR_MISALIGNED = 3,          /* a device pointer is not 16-byte aligned */
     MOE_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < moe_workspace_bytes(...) */
-    MOE_ERR_LAUNCH = 5               /* the HIP runtime refused a launch */
+    MOE_ERR_LAUNCH = 5,              /* the HIP runtime refused a launch */
+    MOE_ERR_SCRATCH_TOO_SMALL = 6    /* moe_layer_forward_noalloc: the call needs more than
+                                        MOE_NOALLOC_SCRATCH_BYTES of scratch */
 } moe_status_t;
 
 /*
@@ -201,6 +203,34 @@ moe_status_t moe_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k
                                const void *w2, void *out,
                                const moe_layer_bufs *bufs, void *ws, size_t ws_bytes,
                                void *stream);
+
+/*
+ * The layer forward for callers that cannot allocate device memory or hand over a
+ * workspace: code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, stages and results as moe_layer_forward (the same
+ * kernels, bit for bit), without ws / ws_bytes: the scratch lives in one static device
+ * array of MOE_NOALLOC_SCRATCH_BYTES per GPU, created when the library's code is loaded on
+ * that GPU and held until the process ends.  Its device address is looked up on the first
+ * call on each device.  The call allocates nothing (no hipMalloc, no library allocation).
+ *   - A call whose layer workspace, moe_workspace_bytes(MOE_WS_LAYER, ...), exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_SCRATCH_TOO_SMALL before enqueuing anything
+ *     (32 MiB: every shape with T * E <= 2^22, e.g. 4096 tokens x 1024 experts, fits; the
+ *     X-MoE Large layer, T = 4096, E = 256, H = 7168, top-8, needs 16.9 MB, mostly the
+ *     gate's partial logits).
+ *   - Every call on one GPU uses that GPU's one array, which keeps the last call's
+ *     contents; each call writes every scratch byte it later reads, so nothing needs
+ *     clearing between calls.  Calls that overlap in time on one GPU (several streams or
+ *     threads) race on the array and must be serialised by the caller.
+ *   - The scratch words moe_layer_forward reports at bytes 0 and 4 of its workspace are
+ *     not reported here (the gate's own routing never has out-of-range ids).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+moe_status_t moe_layer_forward_noalloc(moe_dtype_t dt, int T, int H, int E, int F, int k,
+                                       moe_routing_t routing, const void *x, const void *wg,
+                                       const float *bias, const void *w1, const void *w3,
+                                       const void *w2, void *out,
+                                       const moe_layer_bufs *bufs, void *stream);
 
 /*
  * The layer backward.  The pages present the layer as part of a training system (X-MoE

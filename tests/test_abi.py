@@ -149,6 +149,30 @@ def test_gemm_and_layer_reject(L):
     assert lf(*args(T=0)) == OK
 
 
+def test_layer_forward_noalloc_rejects(L):
+    """The no-workspace layer forward validates like moe_layer_forward and refuses, before
+    touching any device, a call whose layer workspace exceeds its static scratch."""
+    lf = L.moe_layer_forward_noalloc
+    bufs = ops.LayerBufs(*([A] * 10))
+    args = lambda **kw: [kw.get("dt", 1), kw.get("T", 8), kw.get("H", 64), kw.get("E", 4),
+                         kw.get("F", 64), kw.get("k", 2), kw.get("routing", 0), A, A, None, A,
+                         A, A, A, ctypes.byref(kw.get("bufs", bufs)), None]
+    assert lf(*args(k=5)) == UNSUPPORTED
+    assert lf(*args(routing=7)) == INVALID
+    assert lf(*args(F=32)) == UNSUPPORTED
+    assert lf(*args(bufs=ops.LayerBufs(*([A] * 9 + [None])))) == INVALID
+    assert lf(*args(T=0)) == OK
+    # 65536 tokens x 256 experts: 64 MiB of partial logits alone
+    T, H, E, F, k = 65536, 7168, 256, 2048, 8
+    need = ops.moe_workspace_bytes(ops.MOE_WS_LAYER, T, H, E, F, k, ops.MOE_BF16)
+    assert need > ops.MOE_NOALLOC_SCRATCH_BYTES
+    assert lf(*args(T=T, H=H, E=E, F=F, k=k)) == 6
+    assert "MOE_ERR_SCRATCH_TOO_SMALL" in ops.moe_status_string(6)
+    # the X-MoE Large layer fits
+    assert ops.moe_workspace_bytes(ops.MOE_WS_LAYER, 4096, H, E, F, k, ops.MOE_BF16) <= \
+        ops.MOE_NOALLOC_SCRATCH_BYTES
+
+
 def test_layer_backward_rejects(L):
     lb = L.moe_layer_backward
     bufs = ops.LayerBufs(*([A] * 10))
