@@ -60,8 +60,9 @@ size_t gate_ws(int dt, int T, int H, int E) {
 }
 size_t pft_ws(int T, int k, int E) { return round_up(moe::pft_ws_bytes((long long)T * k, E)); }
 size_t gemm_ws(long long N, int E) { return round_up(moe::gemm_ws_bytes(N, E)); }
+size_t pft_layer_ws(int T, int k, int E) { return round_up(moe::pft_layer_ws_bytes(T, k, E)); }
 size_t layer_ws(int dt, int T, int H, int E, int k) {
-    return pft_ws(T, k, E) + gate_ws(dt, T, H, E) + gemm_ws((long long)T * k, E);
+    return pft_layer_ws(T, k, E) + gate_ws(dt, T, H, E) + gemm_ws((long long)T * k, E);
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -111,11 +112,11 @@ MOE_API moe_status_t moe_gate_topk(moe_dtype_t dt, int T, int H, int E, int k,
     if (ws_bytes < gate_ws(dt, T, H, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
     int* refined = static_cast<int*>(ws) + 1;
     float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + kGateHeader);
-    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, refined,
+    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, refined, nullptr, 0,
                                              as_stream(stream))));
     return launched(moe::launch_topk(dt, T, E, k, routing, moe::gate_splits(dt, T, H, E),
                                      partials, bias, x, wg, H, top_experts, top_weights, refined,
-                                     as_stream(stream)));
+                                     nullptr, as_stream(stream)));
 }
 
 MOE_API moe_status_t moe_pft_build(int T, int k, int E, const int32_t* top_experts,
@@ -207,27 +208,40 @@ moe_status_t run_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k
                                const float* bias, const void* w1, const void* w3,
                                const void* w2, void* out, const moe_layer_bufs* b, void* ws,
                                hipStream_t s) {
-    const size_t need_pft = pft_ws(T, k, E), need_gate = gate_ws(dt, T, H, E);
+    const size_t need_pft = pft_layer_ws(T, k, E), need_gate = gate_ws(dt, T, H, E);
     const long long N = (long long)T * k;
     char* w = static_cast<char*>(ws);
     void* ws_pft = w;                       // error word stays at byte 0
     int* refined = reinterpret_cast<int*>(w) + 1;   // beside the error word
     float* partials = reinterpret_cast<float*>(w + need_pft + kGateHeader);
     void* ws_gemm = w + need_pft + need_gate;
-    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, refined, s)));
+    // Buffer build in one launch when the segment counts are small: the gate kernel clears
+    // them, the top-k step adds its picks to them, and the place kernel derives counts,
+    // offsets, the buffer arrays and the GEMM's tile tables from them.
+    const bool fast = moe::pft_layer_fast(T, E);
+    int* hist = fast ? moe::pft_layer_hist(ws_pft, T, k) : nullptr;
+    const int hist_n = fast ? ((T + moe::kPftSegTokens - 1) / moe::kPftSegTokens) * E : 0;
+    const moe::TileTables tables = moe::gemm_tables(ws_gemm, N, E);
+    MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, refined, hist, hist_n,
+                                             s)));
     MOE_TRY(launched(moe::launch_topk(dt, T, E, k, routing, moe::gate_splits(dt, T, H, E),
                                       partials, bias, x, wg, H, b->top_experts, b->top_weights,
-                                      refined, s)));
-    MOE_TRY(launched(moe::launch_pft(T, k, E, b->top_experts, b->counts, b->offsets, b->token_ids,
-                                     b->expert_ids, b->dest_pos, ws_pft, s)));
+                                      refined, hist, s)));
+    if (fast)
+        MOE_TRY(launched(moe::launch_pft_layer(T, k, E, b->top_experts, b->counts, b->offsets,
+                                               b->token_ids, b->expert_ids, b->dest_pos, ws_pft,
+                                               tables, s)));
+    else
+        MOE_TRY(launched(moe::launch_pft(T, k, E, b->top_experts, b->counts, b->offsets,
+                                         b->token_ids, b->expert_ids, b->dest_pos, ws_pft, s)));
     if (b->xd) {
         MOE_TRY(launched(moe::launch_dispatch(dt, T, k, H, x, b->dest_pos, b->xd, s)));
         MOE_TRY(launched(moe::launch_grouped_gemm(dt, (int)N, E, H, F, b->xd, b->offsets, w1, w3,
-                                                  w2, b->h, b->y, ws_gemm, s, b->a, b->g)));
+                                                  w2, b->h, b->y, ws_gemm, s, b->a, b->g, fast)));
     } else {  // dispatch fused into the expert product: rows gathered from x on load
         MOE_TRY(launched(moe::launch_grouped_gemm_gather(dt, (int)N, E, H, F, x, T, b->token_ids,
                                                          b->offsets, w1, w3, w2, b->h, b->y,
-                                                         ws_gemm, s, b->a, b->g)));
+                                                         ws_gemm, s, b->a, b->g, fast)));
     }
     return launched(moe::launch_combine(dt, T, k, H, b->y, b->dest_pos, b->top_weights, out, s));
 }

@@ -32,29 +32,28 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
-// The fp32 logits the layer defines for token t and experts e1, e2: the H products summed
-// in double (each product of two fp32 or bf16 values is exact in double), the bias added
-// in double, then one rounding to fp32.  One wave; every lane returns the same values (the
-// butterfly adds commute).  Each lane issues the loads of kRefChunks 16-byte chunks of the
-// three rows before it uses any, so a pass costs about one memory latency.
+// Share of the exact logits of token t for experts e1 and e2 held by one wave: the products
+// over the 16-byte chunks [c_beg, c_end) of the rows summed in double (each product of two
+// fp32 or bf16 values is exact in double).  Every lane returns the wave's sums (the
+// butterfly adds commute).  Each lane issues the loads of kRefChunks chunks of the three
+// rows before it uses any, so a pass costs about one memory latency.
 constexpr int kRefChunks = 4;
 
 template <typename T>
-__device__ void exact_logits2(const T* __restrict__ x, const T* __restrict__ wg,
-                              const float* __restrict__ bias, int H, int t, int e1, int e2,
-                              int lane, float* v1, float* v2) {
+__device__ void exact_dots2(const T* __restrict__ x, const T* __restrict__ wg, int H, int t,
+                            int e1, int e2, int c_beg, int c_end, int lane, double* d1,
+                            double* d2) {
     constexpr int P = 16 / (int)sizeof(T);
-    const int chunks = H / P;
     const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * H);
     const uint4* w1 = reinterpret_cast<const uint4*>(wg + (size_t)e1 * H);
     const uint4* w2 = reinterpret_cast<const uint4*>(wg + (size_t)e2 * H);
     double s1 = 0.0, s2 = 0.0;
-    for (int c0 = lane; c0 < chunks; c0 += kRefChunks * kWave) {
+    for (int c0 = c_beg + lane; c0 < c_end; c0 += kRefChunks * kWave) {
         uint4 xa[kRefChunks], wa[kRefChunks], wb[kRefChunks];
 #pragma unroll
         for (int u = 0; u < kRefChunks; ++u) {
             const int c = c0 + u * kWave;
-            const bool in = c < chunks;
+            const bool in = c < c_end;
             xa[u] = in ? xr[c] : make_uint4(0, 0, 0, 0);
             wa[u] = in ? w1[c] : make_uint4(0, 0, 0, 0);
             wb[u] = in ? w2[c] : make_uint4(0, 0, 0, 0);
@@ -78,12 +77,8 @@ __device__ void exact_logits2(const T* __restrict__ x, const T* __restrict__ wg,
         s1 += __shfl_xor(s1, m, kWave);
         s2 += __shfl_xor(s2, m, kWave);
     }
-    if (bias) {
-        s1 += static_cast<double>(bias[e1]);
-        s2 += static_cast<double>(bias[e2]);
-    }
-    *v1 = static_cast<float>(s1);
-    *v2 = static_cast<float>(s2);
+    *d1 = s1;
+    *d2 = s2;
 }
 
 // n rounds of wave max over the keys (consumed): lane j < n returns pick j; *last is the
@@ -121,26 +116,34 @@ constexpr float kTieRel = MOE_TIE_REL;
 // logit(t, e) = (partials[0][t][e] + partials[1][t][e] + ...) + bias[e], summed in split
 // order so the result does not depend on scheduling.  Near ties are re-decided exactly:
 // among a token's picks and the first expert left out, any two neighbours closer than
-// kTieRel (relative, at least absolute) get their logits recomputed with exact_logit, and
+// kTieRel (relative, at least absolute) get their logits recomputed as exact sums, and
 // when the last pick and the first one left out are that close, so does every expert
-// within kTieRel of the last pick.  Every other pair is farther apart than twice the
-// fp32 accumulation error, so the final order is that of the exactly rounded logits.
-// Such tokens are counted in *refined.
+// left out within kTieRel of the last pick.  Every other pair is farther apart than twice
+// the fp32 accumulation error, so the final order is that of the exactly rounded logits.
+// The four waves of a block (one token each) share those dot products, a quarter of each
+// row per wave, summed in wave order; such tokens are counted in *refined.
+constexpr int kCandMax = 1024 + kWave;      // candidates of one token: at most E + 1
+
 template <typename T, int NPER, int ROUTE>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(
     const float* __restrict__ partials, const float* __restrict__ bias, int T_, int E, int k,
     int splits, const T* __restrict__ x, const T* __restrict__ wg, int H,
-    int32_t* __restrict__ top_experts, float* __restrict__ top_weights, int* refined) {
-    const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (t >= T_) return;
+    int32_t* __restrict__ top_experts, float* __restrict__ top_weights, int* refined,
+    int* __restrict__ hist) {
+    __shared__ int cand[kWavesPerBlock][kCandMax];
+    __shared__ int ncand[kWavesPerBlock];
+    __shared__ double part[kWavesPerBlock][2];
+    const int wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * kWavesPerBlock + wv;
+    const bool live = t < T_;                  // (no early exit: all waves meet the barriers)
     const int lane = threadIdx.x & 63;
     const size_t stride = (size_t)T_ * E;
-    const float* row = partials + (size_t)t * E;
     uint64_t key[NPER], orig[NPER];
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
         const int e = lane + kWave * i;
-        if (e < E) {
+        if (live && e < E) {
+            const float* row = partials + (size_t)t * E;
             float l = row[e];
             for (int sp = 1; sp < splits; ++sp) l += row[sp * stride + e];
             if (bias) l += bias[e];
@@ -152,67 +155,85 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(
     }
     // the picks and, when there is one, the first expert left out (the (k+1)-th)
     const bool more = k < E;
-    uint64_t last;
-    uint64_t mine = select_top(key, more ? k + 1 : k, lane, &last);
+    uint64_t last = 0, mine = 0;
+    if (live) mine = select_top(key, more ? k + 1 : k, lane, &last);
     // adjacent gaps among them: lane j < k compares pick j with the next one
     const float lj = key_logit(mine);
     const float lup = __shfl(lj, lane + 1 < kWave ? lane + 1 : lane, kWave);
     const float lnext = lane + 1 < k ? lup : key_logit(last);
-    const bool close = (lane + 1 < k || (lane + 1 == k && more)) &&
+    const bool close = live && (lane + 1 < k || (lane + 1 == k && more)) &&
                        (lj - lnext) <= kTieRel * fmaxf(1.0f, fabsf(lj));
     const uint64_t closes = __ballot(close);          // bit j: picks j and j + 1 are close
+    // candidate list: when the last pick and the first one left out are close, every expert
+    // left out within kTieRel of the last pick; then every pick in a close pair
+    const uint64_t below = lanemask_lt();
+    int nc = 0;
     if (closes != 0ull) {
-        // Candidates, refined two at a time (pend: a candidate waiting for a partner):
-        // when the last pick and the first one left out are close, every expert left out
-        // that lies within kTieRel of the last pick; then every pick in a close pair.
-        // (the expert ids are wave-uniform values held in locals, so no cross-lane read
-        // happens inside the one-lane branches below)
-#define MOE_REFINE_PAIR(EA, EB)                                                               \
-        do {                                                                                 \
-            const int ea_ = (EA), eb_ = (EB);                                                \
-            float va_, vb_;                                                                  \
-            exact_logits2(x, wg, bias, H, t, ea_, eb_, lane, &va_, &vb_);                    \
-            _Pragma("unroll") for (int i_ = 0; i_ < NPER; ++i_) {                            \
-                if (lane == (ea_ & 63) && i_ == (ea_ >> 6)) orig[i_] = make_key(va_, ea_);   \
-                if (lane == (eb_ & 63) && i_ == (eb_ >> 6)) orig[i_] = make_key(vb_, eb_);   \
-            }                                                                                \
-        } while (0)
-#define MOE_TAKE(EE)                                                                          \
-        do {                                                                                 \
-            const int ee_ = (EE);                                                            \
-            if (pend < 0) pend = ee_;                                                        \
-            else { MOE_REFINE_PAIR(pend, ee_); pend = -1; }                                  \
-        } while (0)
-        int pend = -1;
         if ((closes >> (k - 1)) & 1ull) {
             const float lk = __shfl(lj, k - 1, kWave);
             const float floor_l = lk - kTieRel * fmaxf(1.0f, fabsf(lk));
 #pragma unroll
             for (int i = 0; i < NPER; ++i) {
                 const int e = lane + kWave * i;
-                uint64_t cand = __ballot(e < E && orig[i] < last && key_logit(orig[i]) >= floor_l);
-                while (cand) {
-                    const int l = __ffsll(static_cast<long long>(cand)) - 1;
-                    cand &= cand - 1;
-                    MOE_TAKE(l + kWave * i);
-                }
+                const bool c = e < E && orig[i] < last && key_logit(orig[i]) >= floor_l;
+                const uint64_t m = __ballot(c);
+                if (c) cand[wv][nc + __popcll(m & below)] = e;
+                nc += __popcll(m);
             }
         }
         const int npick = more ? k + 1 : k;
-        uint64_t need = (closes | (closes << 1)) & (npick < 64 ? ((1ull << npick) - 1) : ~0ull);
-        if (npick > 64 && ((closes >> 63) & 1ull)) {
-            // the first expert left out of 64 picks sits beyond the lanes: take it here
-            MOE_TAKE(static_cast<int>(0xffffffffu - static_cast<uint32_t>(last)));
-        }
+        const uint64_t need = (closes | (closes << 1)) & (npick < 64 ? ((1ull << npick) - 1) : ~0ull);
         const int pe = static_cast<int>(0xffffffffu - static_cast<uint32_t>(mine));
-        while (need) {
-            const int j = __ffsll(static_cast<long long>(need)) - 1;
-            need &= need - 1;
-            MOE_TAKE(__shfl(pe, j, kWave));
+        if ((need >> lane) & 1ull) cand[wv][nc + __popcll(need & below)] = pe;
+        nc += __popcll(need);
+        if (npick > 64 && ((closes >> 63) & 1ull)) {
+            // the first expert left out of 64 picks sits beyond the lanes
+            if (lane == 0) cand[wv][nc] = static_cast<int>(0xffffffffu - static_cast<uint32_t>(last));
+            ++nc;
         }
-        if (pend >= 0) MOE_REFINE_PAIR(pend, pend);
-#undef MOE_TAKE
-#undef MOE_REFINE_PAIR
+    }
+    if (lane == 0) ncand[wv] = nc;
+    __syncthreads();
+    if (ncand[0] + ncand[1] + ncand[2] + ncand[3] > 0) {
+        constexpr int P = 16 / (int)sizeof(T);
+        const int chunks = H / P, q = (chunks + kWavesPerBlock - 1) / kWavesPerBlock;
+        const int c_beg = min(wv * q, chunks), c_end = min(c_beg + q, chunks);
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+            const int nw = ncand[w];
+            const int tw = blockIdx.x * kWavesPerBlock + w;
+            for (int p = 0; p < nw; p += 2) {
+                const int ea = cand[w][p], eb = p + 1 < nw ? cand[w][p + 1] : ea;
+                double da, db;
+                exact_dots2(x, wg, H, tw, ea, eb, c_beg, c_end, lane, &da, &db);
+                if (lane == 0) {
+                    part[wv][0] = da;
+                    part[wv][1] = db;
+                }
+                __syncthreads();
+                if (wv == w) {
+                    double sa = 0.0, sb = 0.0;
+#pragma unroll
+                    for (int u = 0; u < kWavesPerBlock; ++u) {
+                        sa += part[u][0];
+                        sb += part[u][1];
+                    }
+                    if (bias) {
+                        sa += static_cast<double>(bias[ea]);
+                        sb += static_cast<double>(bias[eb]);
+                    }
+                    const float va = static_cast<float>(sa), vb = static_cast<float>(sb);
+#pragma unroll
+                    for (int i = 0; i < NPER; ++i) {
+                        if (lane == (ea & 63) && i == (ea >> 6)) orig[i] = make_key(va, ea);
+                        if (lane == (eb & 63) && i == (eb >> 6)) orig[i] = make_key(vb, eb);
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
+    if (!live) return;
+    if (nc > 0) {
         if (lane == 0 && refined) atomicAdd(refined, 1);
 #pragma unroll
         for (int i = 0; i < NPER; ++i) key[i] = orig[i];
@@ -224,32 +245,36 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(
     if (lane < k) ex = ROUTE == 0 ? expf(lp - l0) : 1.0f / (1.0f + expf(-lp));
     const float z = wave_sum_f32(ex);
     if (lane < k) {
-        top_experts[(size_t)t * k + lane] = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(mine));
+        const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(mine));
+        top_experts[(size_t)t * k + lane] = e;
         top_weights[(size_t)t * k + lane] = ex / z;
+        // the buffer build's per-segment counts (integer adds: the totals do not depend on
+        // the order the atomics land in)
+        if (hist) atomicAdd(&hist[(size_t)(t / kPftSegTokens) * E + e], 1);
     }
 }
 
 template <typename T, int NPER>
 hipError_t launch_topk_n(int T_, int E, int k, int routing, int splits, const float* partials,
                          const float* bias, const void* x, const void* wg, int H, int32_t* te,
-                         float* tw, int* refined, hipStream_t s) {
+                         float* tw, int* refined, int* hist, hipStream_t s) {
     const int blocks = (T_ + kWavesPerBlock - 1) / kWavesPerBlock;
     const T* xt = static_cast<const T*>(x);
     const T* wt = static_cast<const T*>(wg);
     if (routing == 0)
         hipLaunchKernelGGL((topk_kernel<T, NPER, 0>), dim3(blocks), dim3(kWave * kWavesPerBlock), 0, s,
-                           partials, bias, T_, E, k, splits, xt, wt, H, te, tw, refined);
+                           partials, bias, T_, E, k, splits, xt, wt, H, te, tw, refined, hist);
     else
         hipLaunchKernelGGL((topk_kernel<T, NPER, 1>), dim3(blocks), dim3(kWave * kWavesPerBlock), 0, s,
-                           partials, bias, T_, E, k, splits, xt, wt, H, te, tw, refined);
+                           partials, bias, T_, E, k, splits, xt, wt, H, te, tw, refined, hist);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_topk_t(int T_, int E, int k, int routing, int splits, const float* partials,
                          const float* bias, const void* x, const void* wg, int H, int32_t* te,
-                         float* tw, int* refined, hipStream_t s) {
-#define MOE_TOPK(NPER) launch_topk_n<T, NPER>(T_, E, k, routing, splits, partials, bias, x, wg, H, te, tw, refined, s)
+                         float* tw, int* refined, int* hist, hipStream_t s) {
+#define MOE_TOPK(NPER) launch_topk_n<T, NPER>(T_, E, k, routing, splits, partials, bias, x, wg, H, te, tw, refined, hist, s)
     if (E <= 64) return MOE_TOPK(1);
     if (E <= 128) return MOE_TOPK(2);
     if (E <= 256) return MOE_TOPK(4);
@@ -262,10 +287,10 @@ hipError_t launch_topk_t(int T_, int E, int k, int routing, int splits, const fl
 
 hipError_t launch_topk(int dt, int T, int E, int k, int routing, int splits, const float* partials,
                        const float* bias, const void* x, const void* wg, int H, int32_t* te,
-                       float* tw, int* refined, hipStream_t s) {
+                       float* tw, int* refined, int* hist, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    return dt == 0 ? launch_topk_t<float>(T, E, k, routing, splits, partials, bias, x, wg, H, te, tw, refined, s)
-                   : launch_topk_t<bf16_t>(T, E, k, routing, splits, partials, bias, x, wg, H, te, tw, refined, s);
+    return dt == 0 ? launch_topk_t<float>(T, E, k, routing, splits, partials, bias, x, wg, H, te, tw, refined, hist, s)
+                   : launch_topk_t<bf16_t>(T, E, k, routing, splits, partials, bias, x, wg, H, te, tw, refined, hist, s);
 }
 
 }  // namespace moe

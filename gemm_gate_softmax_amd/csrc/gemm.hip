@@ -123,6 +123,8 @@ struct GemmParams {
     int k_slices;           // dense product: k-slices per K split
     int group_tok;          // expert product: token tiles per L2-sharing block (0: kGroupTok)
     int* zero_word;         // dense product: set to 0 by workgroup 0 (nullable)
+    int* zero_buf;          // dense product: zero_buf[0, zero_n) set to 0 (nullable)
+    int zero_n;
 };
 
 // Writes 4 consecutive fp32 partial logits of one token (per-element bounds: E need not be
@@ -524,6 +526,8 @@ template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
 __global__ __launch_bounds__(kThreads, 1) void dense_gemm_kernel(GemmParams<T, NB> p) {
     __shared__ __attribute__((aligned(1024))) char lds[CompTile<BT, BF, NB, S, RB>::kLdsBytes];
     if (blockIdx.x == 0 && threadIdx.x == 0 && p.zero_word) *p.zero_word = 0;
+    for (int i = blockIdx.x * kThreads + threadIdx.x; i < p.zero_n; i += gridDim.x * kThreads)
+        p.zero_buf[i] = 0;
     // work item L = (split, token tile, feature tile), feature tile fastest so the
     // workgroups an XCD runs at once share their activation rows through its L2
     const int ntt = (p.dense_rows + BT - 1) / BT;
@@ -667,75 +671,102 @@ hipError_t launch_expert(const GemmParams<T, NB>& p, int max_m, int max_s, hipSt
     return hipGetLastError();
 }
 
-// Gate logits as K splits: enough (token tile, expert tile, K split) work items to give
-// every CU about four, each split's fp32 partial sums [T][E] written to its own slice of
-// `partials`; the top-k kernel adds them in split order and adds the bias.  (128 x 256
-// tiles over 8 splits measured the same in total: 12 us less here, 5 us more in the top-k,
-// which reads twice the partials.)
-constexpr int kGateBT = 64, kGateBF = 64, kGateStages = 4, kGateRB = 128;
+// Gate logits as K splits: (token tile, expert tile, K split) work items, each split's
+// fp32 partial sums [T][E] written to its own slice of `partials`; the top-k kernel adds
+// them in split order and adds the bias.  A tile covers 64 tokens and up to 256 experts,
+// so x and Wg cross the L2 -> CU path few times (64 x 64 tiles moved 7.5x the operand
+// bytes at X-MoE Large); splits (at most 8) bring the work items to about kGateItems.
+#ifndef MOE_GATE_ITEMS
+#define MOE_GATE_ITEMS 256
+#endif
+#ifndef MOE_GATE_BF_MAX
+#define MOE_GATE_BF_MAX 256
+#endif
+#ifndef MOE_GATE_BT
+#define MOE_GATE_BT 64
+#endif
+constexpr int kGateBT = MOE_GATE_BT, kGateRB = 128, kGateItems = MOE_GATE_ITEMS;
+
+__host__ __device__ inline int gate_bf(int E) {
+    return E <= 64 || MOE_GATE_BF_MAX == 64 ? 64 : (E <= 128 || MOE_GATE_BF_MAX == 128 ? 128 : 256);
+}
 
 __host__ __device__ inline int gate_k_slices(int dt, int T, int H, int E) {
     const int nk = H * (dt == 0 ? 4 : 2) / kGateRB;
-    const int tiles = ((T + kGateBT - 1) / kGateBT) * ((E + kGateBF - 1) / kGateBF);
-    int splits = 1024 / (tiles > 0 ? tiles : 1);
+    const int bf = gate_bf(E);
+    const int tiles = ((T + kGateBT - 1) / kGateBT) * ((E + bf - 1) / bf);
+    int splits = kGateItems / (tiles > 0 ? tiles : 1);
     splits = splits < 1 ? 1 : (splits > 8 ? 8 : splits);
     splits = splits > nk ? nk : splits;
     return (nk + splits - 1) / splits;              // k-slices per split
 }
 
-template <typename T>
-hipError_t gate_logits_t(int dt, int T_, int H, int E, const void* x, const void* wg,
-                         float* partials, int* zero_word, hipStream_t s) {
+template <typename T, int BF, int S>
+hipError_t gate_logits_bf(int dt, int T_, int H, int E, const void* x, const void* wg,
+                          float* partials, int* zero_word, int* zero_buf, int zero_n,
+                          hipStream_t s) {
     GemmParams<T, 1> p{};
     p.zero_word = zero_word;
+    p.zero_buf = zero_buf;
+    p.zero_n = zero_buf ? zero_n : 0;
     p.act = static_cast<const T*>(x);
     p.act_rows = T_;
     p.K = H;
     p.w[0] = static_cast<const T*>(wg);
     p.w_stride = 0;
     p.n_feat = E;
-    p.feat_tiles = (E + kGateBF - 1) / kGateBF;
+    p.feat_tiles = (E + BF - 1) / BF;
     p.dense_rows = T_;
     p.out = partials;
     p.k_slices = gate_k_slices(dt, T_, H, E);
     const int nk = H * (int)sizeof(T) / kGateRB;
     const int splits = (nk + p.k_slices - 1) / p.k_slices;
     const int grid = ((T_ + kGateBT - 1) / kGateBT) * p.feat_tiles * splits;
-    return launch_dense<T, 1, kEpiLogits, kGateBT, kGateBF, kGateStages, kGateRB>(p, grid, s);
+    return launch_dense<T, 1, kEpiLogits, kGateBT, BF, S, kGateRB>(p, grid, s);
 }
 
-struct TableLayout {
-    int* count;
-    int4* table;
-    int4* stable;
-    int cap;
-};
+template <typename T>
+hipError_t gate_logits_t(int dt, int T_, int H, int E, const void* x, const void* wg,
+                         float* partials, int* zero_word, int* zero_buf, int zero_n,
+                         hipStream_t s) {
+    switch (gate_bf(E)) {
+        case 64: return gate_logits_bf<T, 64, 4>(dt, T_, H, E, x, wg, partials, zero_word, zero_buf, zero_n, s);
+        case 128: return gate_logits_bf<T, 128, 4>(dt, T_, H, E, x, wg, partials, zero_word, zero_buf, zero_n, s);
+        default: return gate_logits_bf<T, 256, 3>(dt, T_, H, E, x, wg, partials, zero_word, zero_buf, zero_n, s);
+    }
+}
 
 __host__ __device__ inline long long tiles_cap(long long N, int E) {
     return (N + kExpertBTok - 1) / kExpertBTok + (E < N ? E : N);
 }
 
-inline TableLayout carve_tables(void* ws, int N, int E) {
-    TableLayout t;
+inline TileTables carve_tables(void* ws, long long N, int E) {
+    TileTables t;
     char* w = static_cast<char*>(ws);
     t.count = reinterpret_cast<int*>(w);
     t.cap = (int)tiles_cap(N, E);
     t.table = reinterpret_cast<int4*>(w + 256);
     t.stable = t.table + t.cap;
+    t.btok = kExpertBTok;
+    t.small = kSmallBTok;
     return t;
+}
+
+hipError_t build_tables(const TileTables& tl, const int32_t* offsets, int E, int N, hipStream_t s) {
+    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, N, tl.btok,
+                       tl.small, tl.cap, tl.table, tl.stable, tl.count);
+    return hipGetLastError();
 }
 
 template <typename T>
 hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* gather,
                      int src_rows, const int32_t* offsets, const void* w1, const void* w3,
                      const void* w2, void* h, void* y, void* a, void* g, void* ws,
-                     hipStream_t s) {
+                     bool tables_ready, hipStream_t s) {
     constexpr int BT = kExpertBTok;
-    const TableLayout tl = carve_tables(ws, N, E);
-    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, N, BT, kSmallBTok,
-                       tl.cap, tl.table, tl.stable, tl.count);
+    const TileTables tl = carve_tables(ws, N, E);
     const int max_small = kSmallBTok > 0 ? (E < N ? E : N) : 0;
-    hipError_t err = hipGetLastError();
+    hipError_t err = tables_ready ? hipSuccess : build_tables(tl, offsets, E, N, s);
     if (err != hipSuccess) return err;
 
     constexpr int UP_BF = kExpertUpBF, DN_BF = kExpertDownBF, STAGES = kExpertStages,
@@ -791,10 +822,8 @@ hipError_t grouped_nt_t(int N, int E, int K, int n_feat, const void* act,
                         void* ws, hipStream_t s) {
     constexpr int BT = kExpertBTok, BF = kExpertDownBF, STAGES = kExpertStages,
                   RB = kExpertRowBytes;
-    const TableLayout tl = carve_tables(ws, N, E);
-    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, N, BT, kSmallBTok,
-                       tl.cap, tl.table, tl.stable, tl.count);
-    hipError_t err = hipGetLastError();
+    const TileTables tl = carve_tables(ws, N, E);
+    hipError_t err = build_tables(tl, offsets, E, N, s);
     if (err != hipSuccess) return err;
     const int max_small = kSmallBTok > 0 ? (E < N ? E : N) : 0;
     GemmParams<T, 1> q{};
@@ -821,10 +850,8 @@ hipError_t grouped_pair_t(int N, int E, int H, int F, const void* act, const int
                           void* a, void* g, void* ws, hipStream_t s) {
     constexpr int BT = kExpertBTok, BF = kExpertUpBF, STAGES = kExpertStages,
                   RB = kExpertRowBytes;
-    const TableLayout tl = carve_tables(ws, N, E);
-    hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, E, N, BT, kSmallBTok,
-                       tl.cap, tl.table, tl.stable, tl.count);
-    hipError_t err = hipGetLastError();
+    const TileTables tl = carve_tables(ws, N, E);
+    hipError_t err = build_tables(tl, offsets, E, N, s);
     if (err != hipSuccess) return err;
     const int max_small = kSmallBTok > 0 ? (E < N ? E : N) : 0;
     GemmParams<T, 2> q{};
@@ -921,6 +948,8 @@ size_t gemm_ws_bytes(long long N, int E) {
     return 256 + (size_t)(tiles_cap(N, E) + E) * sizeof(int4);
 }
 
+TileTables gemm_tables(void* ws, long long N, int E) { return carve_tables(ws, N, E); }
+
 int gate_splits(int dt, int T, int H, int E) {
     const int nk = H * (dt == 0 ? 4 : 2) / kGateRB;
     const int per = gate_k_slices(dt, T, H, E);
@@ -928,28 +957,30 @@ int gate_splits(int dt, int T, int H, int E) {
 }
 
 hipError_t launch_gate_logits(int dt, int T, int H, int E, const void* x, const void* wg,
-                              float* partials, int* zero_word, hipStream_t s) {
+                              float* partials, int* zero_word, int* zero_buf, int zero_n,
+                              hipStream_t s) {
     if (T == 0) return hipSuccess;
-    return dt == 0 ? gate_logits_t<float>(dt, T, H, E, x, wg, partials, zero_word, s)
-                   : gate_logits_t<bf16_t>(dt, T, H, E, x, wg, partials, zero_word, s);
+    return dt == 0 ? gate_logits_t<float>(dt, T, H, E, x, wg, partials, zero_word, zero_buf, zero_n, s)
+                   : gate_logits_t<bf16_t>(dt, T, H, E, x, wg, partials, zero_word, zero_buf, zero_n, s);
 }
 
 hipError_t launch_grouped_gemm(int dt, int N, int E, int H, int F, const void* xd,
                                const int32_t* offsets, const void* w1, const void* w3,
                                const void* w2, void* h, void* y, void* ws, hipStream_t s,
-                               void* a, void* g) {
+                               void* a, void* g, bool tables_ready) {
     if (N == 0) return hipSuccess;
-    return dt == 0 ? grouped_t<float>(N, E, H, F, xd, nullptr, 0, offsets, w1, w3, w2, h, y, a, g, ws, s)
-                   : grouped_t<bf16_t>(N, E, H, F, xd, nullptr, 0, offsets, w1, w3, w2, h, y, a, g, ws, s);
+    return dt == 0 ? grouped_t<float>(N, E, H, F, xd, nullptr, 0, offsets, w1, w3, w2, h, y, a, g, ws, tables_ready, s)
+                   : grouped_t<bf16_t>(N, E, H, F, xd, nullptr, 0, offsets, w1, w3, w2, h, y, a, g, ws, tables_ready, s);
 }
 
 hipError_t launch_grouped_gemm_gather(int dt, int N, int E, int H, int F, const void* x, int T,
                                       const int32_t* token_ids, const int32_t* offsets,
                                       const void* w1, const void* w3, const void* w2, void* h,
-                                      void* y, void* ws, hipStream_t s, void* a, void* g) {
+                                      void* y, void* ws, hipStream_t s, void* a, void* g,
+                                      bool tables_ready) {
     if (N == 0) return hipSuccess;
-    return dt == 0 ? grouped_t<float>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, a, g, ws, s)
-                   : grouped_t<bf16_t>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, a, g, ws, s);
+    return dt == 0 ? grouped_t<float>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, a, g, ws, tables_ready, s)
+                   : grouped_t<bf16_t>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, a, g, ws, tables_ready, s);
 }
 
 hipError_t launch_grouped_nt(int dt, int N, int E, int K, int n_feat, const void* act,

@@ -9,23 +9,55 @@
 
 namespace moe {
 
+// The grouped GEMM's tile tables inside its workspace: built by the GEMM launch itself,
+// or, in the layer, by the buffer build (which has the per-expert counts at hand).
+// Experts with more than `small` rows get one `table` entry per btok-row token tile,
+// (expert, index of its first entry, first row, rows); experts with 1..small rows one
+// `stable` entry; count[0], count[1] = entries (table entries capped at cap).
+struct TileTables {
+    int* count;
+    int4* table;
+    int4* stable;
+    int cap;
+    int btok;
+    int small;
+};
+TileTables gemm_tables(void* ws, long long N, int E);
+
 // Gate logits x.Wg^T as gate_splits() fp32 partial sums over K splits, [split][T][E] in
-// `partials` (no bias).  *zero_word (may be NULL) is set to 0 by the launch.
+// `partials` (no bias).  *zero_word (may be NULL) and zero_buf[0, zero_n) are set to 0 by
+// the launch.
 int gate_splits(int dt, int T, int H, int E);
 hipError_t launch_gate_logits(int dt, int T, int H, int E, const void* x, const void* wg,
-                              float* partials, int* zero_word, hipStream_t s);
+                              float* partials, int* zero_word, int* zero_buf, int zero_n,
+                              hipStream_t s);
 // Top-k selection and renormalised weights (routing 0 softmax, 1 sigmoid) from logits =
 // (sum of the partials in split order) + bias; near-tie tokens are re-decided from exact
-// logits recomputed from x and wg, and counted in *refined (may be NULL).
+// logits recomputed from x and wg, and counted in *refined (may be NULL).  With hist (zeroed
+// beforehand), hist[t / kPftSegTokens][e] counts the picks of e among tokens of that block.
 hipError_t launch_topk(int dt, int T, int E, int k, int routing, int splits,
                        const float* partials, const float* bias, const void* x, const void* wg,
                        int H, int32_t* top_experts, float* top_weights, int* refined,
-                       hipStream_t s);
+                       int* hist, hipStream_t s);
 
+// Padding-free buffers.  Workspace: [0] error word, [1] free (the layer keeps the gate's
+// count there), [64 ..) per-segment error counts, then the per-segment histograms.
+constexpr int kPftSegTokens = 64;          // tokens per segment of the layer's buffer build
+constexpr int kPftScanMax = 1 << 14;      // segments x experts of the two-launch builds
 size_t pft_ws_bytes(long long N, int E);
+size_t pft_layer_ws_bytes(int T, int k, int E);
 hipError_t launch_pft(int T, int k, int E, const int32_t* top_experts, int32_t* counts,
                       int32_t* offsets, int32_t* token_ids, int32_t* expert_ids,
                       int32_t* dest_pos, void* ws, hipStream_t s);
+// The layer's histogram (hist of the workspace's layout, filled by launch_topk) -> counts,
+// offsets, the buffer arrays and the GEMM tile tables in one launch; false when the shape
+// is beyond kPftScanMax (then use launch_topk without hist and launch_pft).
+bool pft_layer_fast(int T, int E);
+int* pft_layer_hist(void* ws, int T, int k);
+hipError_t launch_pft_layer(int T, int k, int E, const int32_t* top_experts, int32_t* counts,
+                            int32_t* offsets, int32_t* token_ids, int32_t* expert_ids,
+                            int32_t* dest_pos, void* ws, const TileTables& tables,
+                            hipStream_t s);
 
 hipError_t launch_dispatch(int dt, int T, int k, int H, const void* x, const int32_t* dest_pos,
                            void* xd, hipStream_t s);
@@ -34,17 +66,18 @@ hipError_t launch_combine(int dt, int T, int k, int H, const void* y, const int3
 
 size_t gemm_ws_bytes(long long N, int E);
 // a, g (both or neither, [N][F] each): the up product's two halves are stored beside h.
+// tables_ready: the workspace already holds the tile tables of these offsets.
 hipError_t launch_grouped_gemm(int dt, int N, int E, int H, int F, const void* xd,
                                const int32_t* offsets, const void* w1, const void* w3,
                                const void* w2, void* h, void* y, void* ws, hipStream_t s,
-                               void* a = nullptr, void* g = nullptr);
+                               void* a = nullptr, void* g = nullptr, bool tables_ready = false);
 // The same product with the dispatch fused in: row p of the up product reads x[token_ids[p]]
 // (x has T rows) instead of xd[p]; nothing is written for xd.
 hipError_t launch_grouped_gemm_gather(int dt, int N, int E, int H, int F, const void* x, int T,
                                       const int32_t* token_ids, const int32_t* offsets,
                                       const void* w1, const void* w3, const void* w2, void* h,
                                       void* y, void* ws, hipStream_t s, void* a = nullptr,
-                                      void* g = nullptr);
+                                      void* g = nullptr, bool tables_ready = false);
 
 // ---- backward ----
 // out[p][f] = sum_k act[p][k] * w[e][f][k] over the expert segments (w advances w_stride
