@@ -14,6 +14,7 @@ per-stage table goes to stderr first.
   python bench.py --calibrate-copy     # plain 1 GiB device copies, for HBM byte counters
   python bench.py --up-kernel-only     # one staged layer, then only the up-product calls
                                        # (the launches the traffic counters are read on)
+  python bench.py --dense              # the tile engine vs torch.matmul on dense products
 
 The roofline object covers the dominant kernel, the expert gate/up product with its
 SwiGLU epilogue (two thirds of the layer's flops), timed on its own through the same
@@ -69,6 +70,9 @@ def parse():
                     help="only run plain device copies of 1 GiB (counter calibration)")
     ap.add_argument("--up-kernel-only", action="store_true",
                     help="one staged layer, then --steps calls of the up product alone")
+    ap.add_argument("--dense", action="store_true",
+                    help="the tile engine on dense single-expert products against torch.matmul "
+                         "(hipBLASLt) on the same shapes, as a ceiling reference")
     ap.add_argument("--weight-stream", action="store_true",
                     help="the up product on a routing of one row per expert for every expert of "
                          "the workload: a pure stream of the expert weights (for counter runs)")
@@ -243,6 +247,66 @@ def weight_stream(cfg, args, dev):
     return 0
 
 
+DENSE_SHAPES = (   # (rows, H, F): one expert of the X-MoE Large and Small layers
+    (4096, 7168, 2048), (8192, 7168, 2048), (16384, 7168, 2048), (8192, 2048, 1408),
+    (32768, 2048, 1408))
+
+
+def dense(args, dev):
+    """Dense products (one expert holding every row) through moe_grouped_gemm_swiglu against
+    torch.matmul on the same operands: the up product x.[W1; W3]^T (the engine adds its SwiGLU
+    epilogue) and the down product h.W2^T.  bf16, fp32 accumulate.  torch.matmul is used only
+    as a reference ceiling here; nothing on the library's path calls it."""
+    import torch
+
+    from gemm_gate_softmax_amd import ops
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    rows = []
+    iters = max(4, args.steps)
+    for N, H, F in DENSE_SHAPES:
+        x = torch.randn(N, H, device=dev, generator=gen).to(torch.bfloat16)
+        w1 = (torch.randn(1, F, H, device=dev, generator=gen) / H ** 0.5).to(torch.bfloat16)
+        w3 = (torch.randn(1, F, H, device=dev, generator=gen) / H ** 0.5).to(torch.bfloat16)
+        w2 = (torch.randn(1, H, F, device=dev, generator=gen) / F ** 0.5).to(torch.bfloat16)
+        offs = torch.tensor([0, N], dtype=torch.int32, device=dev)
+        h = torch.empty(N, F, dtype=torch.bfloat16, device=dev)
+        y = torch.empty(N, H, dtype=torch.bfloat16, device=dev)
+        ws = ops.workspace(ops.MOE_WS_GEMM, N, H, 1, F, 1, ops.MOE_BF16, dev)
+        wcat = torch.cat([w1[0], w3[0]], 0).t().contiguous()        # [H, 2F]
+        w2t = w2[0].t().contiguous()                                # [F, H]
+        calls = {
+            "engine_up": lambda: ops.moe_grouped_gemm_swiglu(x, offs, w1, w3, None, h=h, ws=ws),
+            "engine_up_down": lambda: ops.moe_grouped_gemm_swiglu(x, offs, w1, w3, w2, h=h, y=y,
+                                                                  ws=ws),
+            "matmul_up": lambda: torch.matmul(x, wcat),
+            "matmul_down": lambda: torch.matmul(h, w2t),
+        }
+        ms = {}
+        for name, fn in calls.items():
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ms[name] = time_steps(fn, iters, torch.cuda.current_stream())["median"]
+        ms["engine_down"] = ms["engine_up_down"] - ms["engine_up"]
+        fu, fd = 4.0 * N * H * F, 2.0 * N * H * F
+        tf = lambda f, m: round(f / (m * 1e-3) / 1e12, 1)
+        rows.append({"rows": N, "H": H, "F": F,
+                     "up_tflops": {"engine": tf(fu, ms["engine_up"]), "matmul": tf(fu, ms["matmul_up"])},
+                     "down_tflops": {"engine": tf(fd, ms["engine_down"]),
+                                     "matmul": tf(fd, ms["matmul_down"])},
+                     "us": {k_: round(v * 1e3, 1) for k_, v in ms.items()}})
+        log(f"dense {N}x{H}x{F}: up engine {rows[-1]['up_tflops']['engine']} vs matmul "
+            f"{rows[-1]['up_tflops']['matmul']} TFLOP/s; down engine "
+            f"{rows[-1]['down_tflops']['engine']} vs matmul {rows[-1]['down_tflops']['matmul']}")
+        del x, w1, w3, w2, h, y, ws, wcat, w2t
+        torch.cuda.empty_cache()
+    print(json.dumps({"dense": rows, "peak_tflops": MFMA_PEAK_TFLOPS["bf16"],
+                      "note": "median of per-call event intervals; matmul = torch.matmul "
+                              "(hipBLASLt) on the same operands, reference only"}), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -264,6 +328,8 @@ def main():
     ops.lib()                                   # the HIP library or nothing
     if args.weight_stream:
         return weight_stream(cfg, args, dev)
+    if args.dense:
+        return dense(args, dev)
     log(f"bench: {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} F={cfg.F} k={cfg.k} {cfg.dtype}: "
         "drawing inputs on the device")
     d = W.make_device(cfg, seed=args.seed, device=dev)
