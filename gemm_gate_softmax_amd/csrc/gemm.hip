@@ -76,8 +76,9 @@ constexpr int kGroupTokDown = MOE_GROUP_TOK_DOWN;
 #endif
 constexpr bool kInterleave = MOE_INTERLEAVE_READS != 0;
 // In a launch that also streams small experts' weights, a large tile starts its K loop at
-// slice ((ttile + 7 ftile) mod P) * nk / P and wraps around (ttile, ftile: its token and
-// feature tile within the expert).  There the large tiles start at staggered times as CUs
+// slice ((rb + 7 fb) mod P) * nk / P and wraps around (rb: its first row's 128-row block
+// within the expert, fb: its first feature's block of the usual tile width, so tiles of
+// every height sum in the same order).  There the large tiles start at staggered times as CUs
 // free up from tiles of unequal length, and tiles sharing an operand panel then line up
 // their slices in L2 more often; without small tiles, tiles start and run together and the
 // natural order shares best.  The start depends only on the tile, so a gathered
@@ -597,7 +598,11 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, 
         const int ftile = ql / width;
         const int ttile = blk * gtok + (ql - ftile * width);
         const int row0 = seg0 + ttile * BT, row_end = min(seg0 + segn, p.act_rows);
-        const int rot = kRotate && tot_s > 0 ? ((ttile + 7 * ftile) % kRotPeriod) * nk / kRotPeriod : 0;
+        // keyed on the position (128-row block, feature block of the usual width) rather
+        // than the tile index, so tiles of every height sum each output in the same order
+        constexpr int kFeatUnit = NB == 2 ? kExpertUpBF : kExpertDownBF;
+        const int rblk = ttile * BT / 128, fblk = ftile * BF / kFeatUnit;
+        const int rot = kRotate && tot_s > 0 ? ((rblk + 7 * fblk) % kRotPeriod) * nk / kRotPeriod : 0;
         if (row_end - row0 >= BT)
             compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot);
         else
@@ -736,18 +741,28 @@ hipError_t gate_logits_t(int dt, int T_, int H, int E, const void* x, const void
     }
 }
 
-__host__ __device__ inline long long tiles_cap(long long N, int E) {
-    return (N + kExpertBTok - 1) / kExpertBTok + (E < N ? E : N);
+__host__ __device__ inline long long tiles_cap(long long N, int E, int btok = kExpertBTok) {
+    return (N + btok - 1) / btok + (E < N ? E : N);
 }
 
-inline TileTables carve_tables(void* ws, long long N, int E) {
+// Small problems: below kSmallProblemRows routed rows the forward's expert products use
+// 64-token tiles with narrower feature tiles (up 64 features per operand, down 128), so
+// the few tiles there are spread over 4 to 8 times as many SIMDs.  A 128-token tile runs
+// its MFMAs one after another on four SIMDs; with fp32 (4096 flop per 64-cycle MFMA) a
+// 128 x 256 x 256 tile alone takes about 30 us, which set the Tiny layer's time.
+constexpr int kSmallProblemRows = 8192;
+constexpr int kSmallProblemBTok = 64;
+
+inline int fwd_btok(long long N) { return N < kSmallProblemRows ? kSmallProblemBTok : kExpertBTok; }
+
+inline TileTables carve_tables(void* ws, long long N, int E, int btok = kExpertBTok) {
     TileTables t;
     char* w = static_cast<char*>(ws);
     t.count = reinterpret_cast<int*>(w);
-    t.cap = (int)tiles_cap(N, E);
+    t.cap = (int)tiles_cap(N, E, btok);
     t.table = reinterpret_cast<int4*>(w + 256);
     t.stable = t.table + t.cap;
-    t.btok = kExpertBTok;
+    t.btok = btok;
     t.small = kSmallBTok;
     return t;
 }
@@ -758,19 +773,36 @@ hipError_t build_tables(const TileTables& tl, const int32_t* offsets, int E, int
     return hipGetLastError();
 }
 
+// The forward's two products on tiles of BT tokens (up: UP_BF features per operand, down:
+// DN_BF features), over tables of BT-row token tiles.
+template <typename T, int BT, int UP_BF, int DN_BF>
+hipError_t grouped_tiles(int N, int E, int H, int F, const void* xd, const int32_t* gather,
+                         int src_rows, const TileTables& tl, const void* w1, const void* w3,
+                         const void* w2, void* h, void* y, void* a, void* g, hipStream_t s);
+
 template <typename T>
 hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* gather,
                      int src_rows, const int32_t* offsets, const void* w1, const void* w3,
                      const void* w2, void* h, void* y, void* a, void* g, void* ws,
                      bool tables_ready, hipStream_t s) {
-    constexpr int BT = kExpertBTok;
-    const TileTables tl = carve_tables(ws, N, E);
-    const int max_small = kSmallBTok > 0 ? (E < N ? E : N) : 0;
+    const TileTables tl = carve_tables(ws, N, E, fwd_btok(N));
     hipError_t err = tables_ready ? hipSuccess : build_tables(tl, offsets, E, N, s);
     if (err != hipSuccess) return err;
+    if (tl.btok == kSmallProblemBTok)
+        return grouped_tiles<T, kSmallProblemBTok, 64, 128>(N, E, H, F, xd, gather, src_rows, tl,
+                                                            w1, w3, w2, h, y, a, g, s);
+    return grouped_tiles<T, kExpertBTok, kExpertUpBF, kExpertDownBF>(N, E, H, F, xd, gather,
+                                                                     src_rows, tl, w1, w3, w2,
+                                                                     h, y, a, g, s);
+}
 
-    constexpr int UP_BF = kExpertUpBF, DN_BF = kExpertDownBF, STAGES = kExpertStages,
-                  RB = kExpertRowBytes;
+template <typename T, int BT, int UP_BF, int DN_BF>
+hipError_t grouped_tiles(int N, int E, int H, int F, const void* xd, const int32_t* gather,
+                         int src_rows, const TileTables& tl, const void* w1, const void* w3,
+                         const void* w2, void* h, void* y, void* a, void* g, hipStream_t s) {
+    const int max_small = kSmallBTok > 0 ? (E < N ? E : N) : 0;
+    hipError_t err = hipSuccess;
+    constexpr int STAGES = kExpertStages, RB = kExpertRowBytes;
     GemmParams<T, 2> up{};
     up.act = static_cast<const T*>(xd);
     up.act_rows = N;
@@ -945,10 +977,10 @@ hipError_t wgrad_t(int E, int M, int n_feat, int ktot, const void* act, const vo
 }  // namespace
 
 size_t gemm_ws_bytes(long long N, int E) {
-    return 256 + (size_t)(tiles_cap(N, E) + E) * sizeof(int4);
+    return 256 + (size_t)(tiles_cap(N, E, kSmallProblemBTok) + E) * sizeof(int4);
 }
 
-TileTables gemm_tables(void* ws, long long N, int E) { return carve_tables(ws, N, E); }
+TileTables gemm_tables(void* ws, long long N, int E) { return carve_tables(ws, N, E, fwd_btok(N)); }
 
 int gate_splits(int dt, int T, int H, int E) {
     const int nk = H * (dt == 0 ? 4 : 2) / kGateRB;

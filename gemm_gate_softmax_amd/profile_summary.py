@@ -14,6 +14,11 @@
       runs (KiB per dispatch), each scaled by what the same counter reads for a plain
       device copy of B bytes (the copy kernel is the largest dispatch of its run).
 
+  python -m gemm_gate_softmax_amd.profile_summary steps KERNEL_TRACE.csv --command "..."
+        [--first dense_gemm_kernel --last combine_kernel --exclude dispatch_kernel]
+      Per-dispatch durations and the gaps between consecutive dispatches of the layer steps
+      in a kernel trace (medians over the last steps).
+
 Only the standard library is used; nothing here touches the GPU.
 """
 from __future__ import annotations
@@ -141,6 +146,54 @@ def traffic_markdown(a):
     return "\n".join(out)
 
 
+def layer_steps(trace, first, last, exclude=(), max_kernels=16):
+    """The layer steps of a kernel trace: runs of consecutive dispatches that start with a
+    kernel whose name contains `first`, end with one containing `last`, and hold none
+    containing a name in `exclude`.  Each step is a list of (short name, start, end) in ns."""
+    rows = sorted(_rows(trace), key=lambda r: int(r["Start_Timestamp"]))
+    k = [(_short(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+         for r in rows]
+    steps, i = [], 0
+    while i < len(k):
+        if first in k[i][0]:
+            j = i
+            while j < len(k) and j - i < max_kernels and not (j > i and first in k[j][0]):
+                if last in k[j][0]:
+                    break
+                j += 1
+            if j < len(k) and last in k[j][0] and not any(x in n for n, _, _ in k[i:j + 1]
+                                                          for x in exclude):
+                steps.append(k[i:j + 1])
+                i = j + 1
+                continue
+        i += 1
+    return steps
+
+
+def steps_markdown(a):
+    steps = layer_steps(a.trace, a.first, a.last, a.exclude or ())
+    steps = steps[-a.last_steps:] if a.last_steps > 0 else steps
+    if not steps:
+        raise SystemExit("no layer step found in the trace")
+    shape = [n for n, _, _ in steps[-1]]
+    steps = [st for st in steps if [n for n, _, _ in st] == shape]
+    med = statistics.median
+    out = [f"# {a.title}", "", "Command (repository root, one MI355X):", "", f"    {a.command}", "",
+           f"The last {len(steps)} layer steps of the run (dispatches from `{a.first}` through "
+           f"`{a.last}`), medians over the steps; a gap is the time from the end of the previous "
+           "dispatch to the start of this one.", "",
+           "| # | kernel | duration (us) | gap before (us) |", "|---|---|---|---|"]
+    for p, name in enumerate(shape):
+        d = med([(st[p][2] - st[p][1]) / 1e3 for st in steps])
+        g = med([(st[p][1] - st[p - 1][2]) / 1e3 for st in steps]) if p else 0.0
+        out.append(f"| {p} | `{name}` | {d:.1f} | {g:.1f} |")
+    span = med([(st[-1][2] - st[0][1]) / 1e3 for st in steps])
+    busy = med([sum(e - b for _, b, e in st) / 1e3 for st in steps])
+    out += ["", f"Step span {span:.1f} us: kernels {busy:.1f} us, gaps {span - busy:.1f} us "
+            f"({len(shape)} dispatches)."]
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -156,9 +209,21 @@ def main(argv=None):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--command", action="append", required=True)
+    g = sub.add_parser("steps")
+    g.add_argument("trace")
+    g.add_argument("--command", required=True)
+    g.add_argument("--title", default="Layer steps: kernel durations and launch gaps")
+    g.add_argument("--first", default="dense_gemm_kernel")
+    g.add_argument("--last", default="combine_kernel")
+    g.add_argument("--exclude", action="append")
+    g.add_argument("--last-steps", type=int, default=20)
     a = ap.parse_args(argv)
-    sys.stdout.write(stats_markdown(a.csv, a.command, a.title, a.trace, a.kernel, a.last)
-                     if a.cmd == "stats" else traffic_markdown(a))
+    if a.cmd == "stats":
+        sys.stdout.write(stats_markdown(a.csv, a.command, a.title, a.trace, a.kernel, a.last))
+    elif a.cmd == "traffic":
+        sys.stdout.write(traffic_markdown(a))
+    else:
+        sys.stdout.write(steps_markdown(a))
     return 0
 
 

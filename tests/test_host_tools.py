@@ -74,3 +74,30 @@ def test_last_dispatches_of_a_kernel(tmp_path):
         for name, s, d in (("k_a<1>(int)", 100, 5000), ("k_b(int)", 200, 9000),
                            ("k_a<1>(int)", 300, 7000), ("k_a<1>(int)", 50, 1000))])
     assert ps.last_dispatches(trace, "k_a", 2) == [5.0, 7.0]
+
+
+def test_layer_steps_durations_and_gaps(tmp_path):
+    # two layer steps (a, b, c) with a 2 us and a 3 us gap, one unrelated kernel between,
+    # and one step holding an excluded kernel
+    rows, t = [], 0
+    def k(name, dur, gap):
+        nonlocal t
+        t += gap
+        rows.append({"Kernel_Name": name + "(int)", "Start_Timestamp": t, "End_Timestamp": t + dur})
+        t += dur
+    for _ in range(2):
+        k("first_k", 10000, 1000)
+        k("mid_k", 5000, 2000)
+        k("last_k", 7000, 3000)
+        k("other", 1000, 500)
+    k("first_k", 10000, 1000)
+    k("skip_me", 1000, 0)
+    k("last_k", 7000, 0)
+    trace = _csv(tmp_path / "t.csv", rows)
+    steps = ps.layer_steps(trace, "first_k", "last_k", exclude=("skip_me",))
+    assert len(steps) == 2 and [n for n, _, _ in steps[0]] == ["first_k(int)", "mid_k(int)", "last_k(int)"]
+    a = argparse.Namespace(trace=trace, first="first_k", last="last_k", exclude=["skip_me"],
+                           last_steps=20, title="t", command="c")
+    md = ps.steps_markdown(a)
+    assert "| 1 | `mid_k(int)` | 5.0 | 2.0 |" in md and "| 2 | `last_k(int)` | 7.0 | 3.0 |" in md
+    assert "Step span 27.0 us: kernels 22.0 us, gaps 5.0 us" in md
