@@ -96,7 +96,7 @@ def recorded_traffic(workload):
     fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, re.M))
     if fields.get("workload") != workload or fields.get("source_sha256") != kernel_digest():
         return None
-    return int(fields["hbm_bytes_per_launch"])
+    return int(fields["fabric_bytes_per_launch"])
 
 
 def calibrate_copy():

@@ -19,6 +19,11 @@
       Per-dispatch durations and the gaps between consecutive dispatches of the layer steps
       in a kernel trace (medians over the last steps).
 
+  python -m gemm_gate_softmax_amd.profile_summary counters PASS1.csv [PASS2.csv ...] \\
+      --kernel PREFIX --last N --command "..." [--command "..."]
+      Mean per dispatch of every counter of ``rocprofv3 --pmc`` passes over the last N
+      dispatches of one kernel.
+
 Only the standard library is used; nothing here touches the GPU.
 """
 from __future__ import annotations
@@ -124,7 +129,7 @@ def traffic_markdown(a):
     fetch_b = statistics.mean(fetch) * 1024.0 * f_scale
     write_b = statistics.mean(write) * 1024.0 * w_scale
     total = int(round(fetch_b + write_b))
-    out = [f"# HBM traffic per launch: {a.kernel} ({a.workload})", "",
+    out = [f"# L2<->fabric bytes per launch: {a.kernel} ({a.workload})", "",
            "Commands (repository root, one MI355X), one counter per run:", ""]
     out += [f"    {c}" for c in a.command]
     out += ["",
@@ -142,7 +147,10 @@ def traffic_markdown(a):
             f"- source_sha256: `{kernel_digest()}`",
             f"- fetch_scale: `{f_scale:.6f}`",
             f"- write_scale: `{w_scale:.6f}`",
-            f"- hbm_bytes_per_launch: `{total}`", ""]
+            f"- fabric_bytes_per_launch: `{total}`", "",
+            "FETCH_SIZE and WRITE_SIZE count what the L2 exchanged with the memory fabric; the",
+            "fabric's own cache (MALL) may serve part of it, so these are fabric bytes, an upper",
+            "bound on HBM bytes.", ""]
     return "\n".join(out)
 
 
@@ -194,6 +202,32 @@ def steps_markdown(a):
     return "\n".join(out) + "\n"
 
 
+def counter_means(path, prefix, last):
+    """Mean per dispatch (each counter summed over its instances) over the last `last`
+    dispatches of kernels whose name contains prefix: {counter: mean}."""
+    per = {}
+    for r in _rows(path):
+        if prefix in _short(r["Kernel_Name"], 10**6):
+            d = int(r["Dispatch_Id"])
+            per.setdefault(d, {})
+            per[d][r["Counter_Name"]] = per[d].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(per)[-last:]
+    names = sorted({n for d in ids for n in per[d]})
+    return {n: statistics.mean(per[d].get(n, 0.0) for d in ids) for n in names}, len(ids)
+
+
+def counters_markdown(a):
+    out = [f"# {a.title}", "", "Commands (repository root, one MI355X), one pass each:", ""]
+    out += [f"    {c}" for c in a.command]
+    out += ["", f"Each counter summed over its instances, mean over the last {a.last} dispatches "
+            f"of `{a.kernel}`.", "", "| counter | per dispatch |", "|---|---|"]
+    for path in a.csv:
+        means, n = counter_means(path, a.kernel, a.last)
+        for name, v in means.items():
+            out.append(f"| {name} | {v:.4g} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -217,7 +251,16 @@ def main(argv=None):
     g.add_argument("--last", default="combine_kernel")
     g.add_argument("--exclude", action="append")
     g.add_argument("--last-steps", type=int, default=20)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--last", type=int, default=5)
+    c.add_argument("--title", default="Hardware counters")
+    c.add_argument("--command", action="append", required=True)
     a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        sys.stdout.write(counters_markdown(a))
+        return 0
     if a.cmd == "stats":
         sys.stdout.write(stats_markdown(a.csv, a.command, a.title, a.trace, a.kernel, a.last))
     elif a.cmd == "traffic":
