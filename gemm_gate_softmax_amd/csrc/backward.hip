@@ -12,10 +12,10 @@
 //   gate:     dl from dw through the routing weights of the picked logits (softmax over the
 //             picks, or normalised sigmoids), dx[t] += sum_j dl_j Wg[e_j],
 //             dWg = DL^T x, dbias = column sums of DL (DL [T][E] holds dl at the picks)
-// Every product runs on the NT tile GEMM of gemm.hip: weights are transposed per active
-// expert, and the weight gradients read activations transposed into per-expert column
-// blocks aligned to 64 and zero padded, so each expert's gradient is one GEMM over its own
-// K range.  All accumulation is fp32; every gradient tensor is rounded once to its storage
+// Every product runs on the tile GEMM of gemm.hip: dh and dxd read the stored weights
+// K-major (transposed in the LDS fragment read), and the weight gradients read activations
+// transposed into per-expert column blocks aligned to 64 and zero padded, so each expert's
+// gradient is one GEMM over its own K range.  All accumulation is fp32; every gradient tensor is rounded once to its storage
 // type (dbias, dw and dl stay fp32).  Deterministic: no atomics.
 #include "device.h"
 #include "launch.h"
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict
     dag[p * 2 * fchunks + fchunks + fc] = pack16(dg, T{});
 }
 
-// ---- transposes (64 x 64 tiles through LDS, 16-byte global accesses) ----
+// ---- segment transposes (64 x 64 tiles through LDS, 16-byte global accesses) ----
 // Every transposed dimension here is a multiple of 64, so tiles are whole.  A thread reads
 // 16-byte chunks of source rows into LDS (one 32-bit word per element, rows padded by one
 // word), then gathers 16 bytes of a destination row from consecutive source rows.
@@ -270,34 +270,6 @@ struct TileIO {
         return pack16(f, T{});
     }
 };
-
-// Per expert e (grid z): out[e][c][col0 + r] = in[e][r][c] for r < R, c < C (both multiples
-// of 64); experts with counts[e] == 0 are skipped when counts is not NULL.
-template <typename T>
-__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, T* __restrict__ out,
-                                                        int R, int C, long long in_es,
-                                                        long long out_es, int out_ld, int col0,
-                                                        const int32_t* __restrict__ counts) {
-    using IO = TileIO<T>;
-    constexpr int kPer = IO::kPer, kCpr = kTile / kPer;
-    __shared__ uint32_t tile[kTile][kTile + 1];
-    const int e = blockIdx.z;
-    if (counts && counts[e] == 0) return;
-    const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
-    const T* src = in + (size_t)e * in_es;
-    for (int i = threadIdx.x; i < IO::kChunks; i += 256) {
-        const int r = i / kCpr, cc = i - r * kCpr;
-        IO::put(tile, r, cc * kPer,
-                *reinterpret_cast<const uint4*>(src + (size_t)(r0 + r) * C + c0 + cc * kPer));
-    }
-    __syncthreads();
-    T* dst = out + (size_t)e * out_es;
-    for (int i = threadIdx.x; i < IO::kChunks; i += 256) {
-        const int c = i / kCpr, rr = i - c * kCpr;
-        *reinterpret_cast<uint4*>(dst + (size_t)(c0 + c) * out_ld + col0 + r0 + rr * kPer) =
-            IO::get(tile, rr * kPer, c);
-    }
-}
 
 // Segment transpose: out[c][q] = in[src(q)][c] for q < kmax, with src(q) = row pmap[q]
 // (through gather when not NULL) or zero where pmap[q] < 0; pmap NULL: q itself for q < R.
@@ -432,16 +404,6 @@ __global__ __launch_bounds__(256) void pmap_kernel(const int32_t* __restrict__ o
 }
 
 template <typename T>
-hipError_t transpose_experts(const void* in, void* out, int E, int R, int C, long long in_es,
-                             long long out_es, int out_ld, int col0, const int32_t* counts,
-                             hipStream_t s) {
-    const dim3 grid((C + kTile - 1) / kTile, (R + kTile - 1) / kTile, E);
-    hipLaunchKernelGGL(transpose_kernel<T>, grid, dim3(256), 0, s, static_cast<const T*>(in),
-                       static_cast<T*>(out), R, C, in_es, out_es, out_ld, col0, counts);
-    return hipGetLastError();
-}
-
-template <typename T>
 hipError_t seg_transpose(const void* in, int C, const int32_t* gather, const int32_t* pmap, int R,
                          int kmax, void* out, hipStream_t s) {
     const dim3 grid((kmax + kTile - 1) / kTile, (C + kTile - 1) / kTile);
@@ -454,7 +416,7 @@ size_t align_up(size_t v) { return (v + 255) / 256 * 256; }
 
 // Workspace layout of the layer backward (every piece 256-byte aligned).
 struct BwdWs {
-    void *gemm, *w2t, *w13t, *dy, *dh, *a, *g, *dag, *dxd, *dyt, *ht, *xdt, *dagt, *dlt, *xt;
+    void *gemm, *dy, *dh, *a, *g, *dag, *dxd, *dyt, *ht, *xdt, *dagt, *dlt, *xt;
     float *dw, *dl;
     int32_t *kofs, *pmap, *gofs, *elist, *nlist;
     int kmax, tpad;
@@ -475,8 +437,6 @@ BwdWs carve_bwd(void* base, int dt, int T, int H, int E, int F, int k) {
         return r;
     };
     w.gemm = take(gemm_ws_bytes(N, E));
-    w.w2t = take(es * E * F * H);
-    w.w13t = take(es * E * H * 2 * F);
     w.dy = take(es * N * H);
     w.dh = take(es * N * F);
     w.a = take(es * N * F);
@@ -525,16 +485,10 @@ hipError_t layer_backward_t(const BwdParams& b, hipStream_t s) {
                        static_cast<const uint4*>(b.dout), static_cast<const uint4*>(b.y), b.dest_pos,
                        b.top_weights, static_cast<uint4*>(w.dy), dw, k, N, chunks_h);
     MOE_CHECK(hipGetLastError());
-    // transposed weights of the active experts: W2t [E][F][H], W13t [E][H][2F]
-    MOE_CHECK(transpose_experts<T>(b.w2, w.w2t, E, H, F, (long long)H * F, (long long)F * H, H, 0,
-                                   b.counts, s));
-    MOE_CHECK(transpose_experts<T>(b.w1, w.w13t, E, F, H, (long long)F * H, (long long)H * 2 * F,
-                                   2 * F, 0, b.counts, s));
-    MOE_CHECK(transpose_experts<T>(b.w3, w.w13t, E, F, H, (long long)F * H, (long long)H * 2 * F,
-                                   2 * F, F, b.counts, s));
-    // dh = dy . W2[e];  a, g recomputed;  dag = SwiGLU backward;  dxd = dag . [W1; W3]
-    MOE_CHECK(launch_grouped_nt(dt, N, E, H, F, w.dy, b.offsets, w.w2t, (long long)F * H, w.dh,
-                                w.gemm, s));
+    // dh = dy . W2[e];  a, g recomputed;  dag = SwiGLU backward;  dxd = dag . [W1; W3].  The
+    // weights are read as stored (W2[e] is [H][F], W1[e] and W3[e] are [F][H]: K-major here).
+    MOE_CHECK(launch_grouped_kmajor(dt, N, E, H, F, w.dy, b.offsets, b.w2, nullptr, 0, F,
+                                    (long long)H * F, w.dh, w.gemm, s));
     const void* act = b.xd ? b.xd : b.x;
     const int32_t* gather = b.xd ? nullptr : b.token_ids;
     // a and g: stored by the forward, or recomputed (the same tiles and summation order)
@@ -549,8 +503,8 @@ hipError_t layer_backward_t(const BwdParams& b, hipStream_t s) {
                        static_cast<const uint4*>(w.dh), static_cast<const uint4*>(ag_a),
                        static_cast<const uint4*>(ag_g), nfc, fchunks, static_cast<uint4*>(w.dag));
     MOE_CHECK(hipGetLastError());
-    MOE_CHECK(launch_grouped_nt(dt, N, E, 2 * F, H, w.dag, b.offsets, w.w13t,
-                                (long long)H * 2 * F, w.dxd, w.gemm, s));
+    MOE_CHECK(launch_grouped_kmajor(dt, N, E, 2 * F, H, w.dag, b.offsets, b.w1, b.w3, F, H,
+                                    (long long)F * H, w.dxd, w.gemm, s));
     // per-expert column blocks for the weight gradients
     hipLaunchKernelGGL(kofs_kernel, dim3(1), dim3(1024), 0, s, b.counts, E, w.kofs);
     MOE_CHECK(hipGetLastError());

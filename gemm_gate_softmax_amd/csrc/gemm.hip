@@ -123,6 +123,9 @@ struct GemmParams {
     void* out3;             // kEpiSwiGLUPair: g
     int k_slices;           // dense product: k-slices per K split
     int group_tok;          // expert product: token tiles per L2-sharing block (0: kGroupTok)
+    long long w_ld;         // K-major weights: elements from one k row to the next
+    int w_k2;               // K-major weights: first k-slice read from the second tensor
+    long long w_k2_adj;     // bytes added to weight addresses from k-slice w_k2 on
     int* zero_word;         // dense product: set to 0 by workgroup 0 (nullable)
     int* zero_buf;          // dense product: zero_buf[0, zero_n) set to 0 (nullable)
     int zero_n;
@@ -223,6 +226,51 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
     return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
+// K-major weights (the backward's dh = dy W2[e] and dxd = da W1[e] + dg W3[e] contract over
+// the row index of the stored weights): a stage holds each k-slice as n-blocks of KPS = RB /
+// sizeof(T) features, KPS k rows per n-block, each row the block's KPS features of one k
+// (RB bytes, 16-byte chunks permuted by kmajor_swizzle).  The direct-to-LDS transfers stay
+// whole-row copies; the transpose happens in the fragment read.
+__device__ __forceinline__ int kmajor_swizzle(int k) { return ((k >> 1) & 1) << 2; }
+
+typedef short moe_v4s_t __attribute__((ext_vector_type(4)));
+
+// This lane's weight fragment of a K-major region for features [mrow, mrow + 32) (mrow a
+// multiple of 32) and k-step KSTEP: what the K-contiguous layout's 16-byte read gives, i.e.
+// 8 consecutive k (bf16) or 4 (fp32, element e for the e-th MFMA) of feature mrow + l % 32.
+// bf16 uses the gfx950 LDS transpose read: in each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte pieces addressed by lanes 4j + i / 4 (j = 0..3), so lane L of a group
+// addresses features 4 (L % 4) .. +3 of k row L / 4, and lane i gets 4 consecutive k of one
+// feature; two reads give the 8 k of the MFMA's operand.  fp32 reads its 4 k one by one.
+template <typename T, int RB>
+__device__ __forceinline__ uint4 kmajor_frag(const char* region, int mrow, int kstep, int lane) {
+    constexpr int KPS = RB / (int)sizeof(T);
+    if constexpr (sizeof(T) == 2) {
+        const int g = lane >> 4, L = lane & 15;
+        const int n = mrow + 16 * (g & 1) + 4 * (L & 3);
+        const int nb = n / KPS, nn = n % KPS;
+        const int k = 16 * kstep + 8 * (g >> 1) + (L >> 2);
+        const char* a = region + (nb * KPS + k) * RB + (((nn >> 3) ^ kmajor_swizzle(k)) << 4) + (nn & 7) * 2;
+        typedef __attribute__((address_space(3))) moe_v4s_t lds_v4s;
+        const moe_v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(a));
+        const moe_v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(a + 4 * RB));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        return make_uint4(l2.x, l2.y, h2.x, h2.y);
+    } else {
+        const int l32 = lane & 31, lhalf = lane >> 5;
+        const int n = mrow + l32;
+        const int nb = n / KPS, nn = n % KPS;
+        uint32_t v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k = 8 * kstep + 4 * lhalf + e;
+            v[e] = *reinterpret_cast<const uint32_t*>(
+                region + (nb * KPS + k) * RB + (((nn >> 2) ^ kmajor_swizzle(k)) << 4) + (nn & 3) * 4);
+        }
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    }
+}
+
 // One tile: activation rows [row0, row0 + BT) (stored below row_end) against weight rows
 // [f0, f0 + BF) of each operand of `expert`, by a workgroup of 8 waves in two roles.
 // Waves 4..7 only move data: each issues its share of every stage's direct-to-LDS
@@ -234,8 +282,10 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
 // land and every compute wave has finished reading stage kt-1, so after it stage kt is
 // read while stage kt+S-1 is loaded into the slot stage kt-1 left.  WNT marks the weight
 // transfers non-temporal: for a tile that is the only reader of its weights.  The tile
-// visits k-slices rot, rot+1, ..., nk-1, 0, ..., rot-1 of its K range (rot < nk).
-template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool FULL, bool WNT = false>
+// visits k-slices rot, rot+1, ..., nk-1, 0, ..., rot-1 of its K range (rot < nk).  WKM:
+// the weights are stored K-major (w[b][k][n], rows w_ld apart), see kmajor_frag.
+template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool FULL, bool WNT = false,
+          bool WKM = false>
 __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* lds, int expert,
                                              int row0, int row_end, int f0, int s0, int nk,
                                              int rot = 0) {
@@ -274,6 +324,15 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
                 int ar = min(row0 + r, p.act_rows - 1);
                 if (p.gather) ar = min(max(p.gather[ar], 0), p.src_rows - 1);   // fused dispatch
                 src[i] = reinterpret_cast<const char*>(p.act) + (size_t)ar * row_bytes + k_off + c * 16;
+            } else if constexpr (WKM) {
+                // k row kr of n-block nb of operand b; this slot holds its chunk cw
+                constexpr int KPS = kRowBytes / (int)sizeof(T), kPer = 16 / (int)sizeof(T);
+                const int b = (kBlkRows * i - BT) / BF;
+                const int rr = r - BT - b * BF, nb = rr / KPS, kr = rr % KPS;
+                const int cw = (lane % kChunks) ^ kmajor_swizzle(kr);
+                const int n = min(f0 + nb * KPS + cw * kPer, p.n_feat - kPer);
+                src[i] = reinterpret_cast<const char*>(p.w[b] + (size_t)expert * p.w_stride +
+                                                       ((size_t)s0 * KPS + kr) * p.w_ld + n);
             } else {
                 const int b = (kBlkRows * i - BT) / BF;
                 const int f = min(f0 + (r - BT) - b * BF, p.n_feat - 1);
@@ -296,14 +355,19 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
                               : min(max((min(row_end - row0, BT) - lw * kRowsPerDma + kBlkRows - 1) /
                                             kBlkRows, 0), kActDma);
         const int keff = kDma - (kActDma - nact);                     // transfers per slice
+        // K-major weights advance by KPS rows per k-slice (and switch tensors at w_k2)
+        const long long wslice = WKM ? (long long)(kRowBytes / (int)sizeof(T)) * p.w_ld * (long long)sizeof(T) : 0;
 #define MOE_ISSUE(KT, SLOT)                                                                   \
         do {                                                                                 \
             const uint32_t b_ = __builtin_amdgcn_readfirstlane(wbase + (SLOT) * kStageBytes); \
             const int ks_ = (KT) + rot;                                                      \
-            const size_t o_ = (size_t)(ks_ >= nk ? ks_ - nk : ks_) * kRowBytes;              \
+            const int kk_ = ks_ >= nk ? ks_ - nk : ks_;                                      \
+            const size_t o_ = (size_t)kk_ * kRowBytes;                                       \
+            const long long ow_ = WKM ? kk_ * wslice + (kk_ >= p.w_k2 ? p.w_k2_adj : 0) : (long long)o_; \
             _Pragma("unroll") for (int i_ = 0; i_ < kDma; ++i_)                              \
-                if (i_ >= kActDma && WNT) dma16_nt(src[i_] + o_, b_ + i_ * 4096);           \
-                else if (i_ >= kActDma || i_ < nact) dma16(src[i_] + o_, b_ + i_ * 4096);     \
+                if (i_ >= kActDma && WNT) dma16_nt(src[i_] + ow_, b_ + i_ * 4096);          \
+                else if (i_ >= kActDma) dma16(src[i_] + ow_, b_ + i_ * 4096);               \
+                else if (i_ < nact) dma16(src[i_] + o_, b_ + i_ * 4096);                    \
         } while (0)
         if (nk == 1) {
             // a single k-slice (weight gradients of experts with at most 64 rows): no
@@ -370,8 +434,12 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
         _Pragma("unroll") for (int j = 0; j < TT; ++j) FA[j] =                               \
             *reinterpret_cast<const uint4*>(st_ + (wt * (BT / 2) + j * 32 + l32) * kRowBytes + cs_); \
         _Pragma("unroll") for (int b = 0; b < NB; ++b)                                       \
-            _Pragma("unroll") for (int i = 0; i < FT; ++i) FW[b][i] = *reinterpret_cast<const uint4*>( \
-                st_ + (BT + b * BF + wf * (BF / 2) + i * 32 + l32) * kRowBytes + cs_);      \
+            _Pragma("unroll") for (int i = 0; i < FT; ++i) {                                 \
+                if constexpr (WKM) FW[b][i] = kmajor_frag<T, RB>(st_ + (BT + b * BF) * kRowBytes, \
+                                                               wf * (BF / 2) + i * 32, (KSTEP), lane); \
+                else FW[b][i] = *reinterpret_cast<const uint4*>(                             \
+                    st_ + (BT + b * BF + wf * (BF / 2) + i * 32 + l32) * kRowBytes + cs_);  \
+            }                                                                                \
     } while (0)
     // Scheduling hint (bf16, one MFMA instruction per fragment pair): one fragment read after
     // each MFMA, so reads issue while the MFMA pipe is busy rather than as a block between
@@ -570,7 +638,7 @@ constexpr int expert_lds_bytes() {
     return a > b ? a : b;
 }
 
-template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
+template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool WKM = false>
 __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, NB> p) {
     __shared__ __attribute__((aligned(1024))) char lds[expert_lds_bytes<BT, BF, NB, S, RB>()];
     const int tot_m = p.table_count[0] * p.feat_tiles;
@@ -604,9 +672,9 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, 
         const int rblk = ttile * BT / 128, fblk = ftile * BF / kFeatUnit;
         const int rot = kRotate && tot_s > 0 ? ((rblk + 7 * fblk) % kRotPeriod) * nk / kRotPeriod : 0;
         if (row_end - row0 >= BT)
-            compute_tile<T, NB, EPI, BT, BF, S, RB, true>(p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot);
+            compute_tile<T, NB, EPI, BT, BF, S, RB, true, false, WKM>(p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot);
         else
-            compute_tile<T, NB, EPI, BT, BF, S, RB, false>(p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot);
+            compute_tile<T, NB, EPI, BT, BF, S, RB, false, false, WKM>(p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot);
     } else if constexpr (kSmallBTok > 0) {
         constexpr int SB = kSmallBTok > 0 ? kSmallBTok : 64;
         const int Ls = xcd * chunk_s + (j - a0);
@@ -614,9 +682,9 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, 
         const int ftile = Ls - (Ls / p.feat_tiles) * p.feat_tiles;
         const int row0 = te.z, row_end = min(te.z + te.w, p.act_rows);
         if (row_end - row0 >= SB)
-            compute_tile<T, NB, EPI, SB, BF, kSmallStages, RB, true, true>(p, lds, te.x, row0, row_end, ftile * BF, 0, nk);
+            compute_tile<T, NB, EPI, SB, BF, kSmallStages, RB, true, true, WKM>(p, lds, te.x, row0, row_end, ftile * BF, 0, nk);
         else
-            compute_tile<T, NB, EPI, SB, BF, kSmallStages, RB, false, true>(p, lds, te.x, row0, row_end, ftile * BF, 0, nk);
+            compute_tile<T, NB, EPI, SB, BF, kSmallStages, RB, false, true, WKM>(p, lds, te.x, row0, row_end, ftile * BF, 0, nk);
     }
 }
 
@@ -668,11 +736,11 @@ hipError_t launch_dense(const GemmParams<T, NB>& p, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
+template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool WKM = false>
 hipError_t launch_expert(const GemmParams<T, NB>& p, int max_m, int max_s, hipStream_t s) {
     const int grid = 8 * ((max_m + 7) / 8 + (max_s + 7) / 8);
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((expert_gemm_kernel<T, NB, EPI, BT, BF, S, RB>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((expert_gemm_kernel<T, NB, EPI, BT, BF, S, RB, WKM>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -846,14 +914,18 @@ hipError_t grouped_tiles(int N, int E, int H, int F, const void* xd, const int32
 }
 
 // ---- backward products ----
-// Generic grouped NT product over the expert segments: out[p][f] = sum_k act[p][k] *
-// w[e][f][k] for rows p of expert e, with the forward's tile table and the 128 x 256 tile.
+// Grouped product over the expert segments with K-major weights: out[p][n] = sum_k act[p][k]
+// * W_e[k][n] for the rows p of expert e, where row k of W_e is row k of w_lo[e] for k <
+// k_split and row k - k_split of w_hi[e] from there on (w_ld elements per row, w_stride per
+// expert).  The weights are read as stored: no transposed copies.  The forward's tile table
+// and the 128 x 256 tile.
 template <typename T>
-hipError_t grouped_nt_t(int N, int E, int K, int n_feat, const void* act,
-                        const int32_t* offsets, const void* w, long long w_stride, void* out,
-                        void* ws, hipStream_t s) {
+hipError_t grouped_kmajor_t(int N, int E, int K, int n_feat, const void* act,
+                            const int32_t* offsets, const void* w_lo, const void* w_hi,
+                            int k_split, long long w_ld, long long w_stride, void* out, void* ws,
+                            hipStream_t s) {
     constexpr int BT = kExpertBTok, BF = kExpertDownBF, STAGES = kExpertStages,
-                  RB = kExpertRowBytes;
+                  RB = kExpertRowBytes, KPS = RB / (int)sizeof(T);
     const TileTables tl = carve_tables(ws, N, E);
     hipError_t err = build_tables(tl, offsets, E, N, s);
     if (err != hipSuccess) return err;
@@ -862,16 +934,25 @@ hipError_t grouped_nt_t(int N, int E, int K, int n_feat, const void* act,
     q.act = static_cast<const T*>(act);
     q.act_rows = N;
     q.K = K;
-    q.w[0] = static_cast<const T*>(w);
+    q.w[0] = static_cast<const T*>(w_lo);
     q.w_stride = w_stride;
+    q.w_ld = w_ld;
+    q.w_k2 = 1 << 30;
+    if (w_hi != nullptr) {
+        // from k-slice w_k2 on, addresses computed from w_lo land in w_hi
+        const long long wslice = (long long)KPS * w_ld * (long long)sizeof(T);
+        q.w_k2 = k_split / KPS;
+        q.w_k2_adj = (long long)(reinterpret_cast<uintptr_t>(w_hi) - reinterpret_cast<uintptr_t>(w_lo)) -
+                     q.w_k2 * wslice;
+    }
     q.n_feat = n_feat;
     q.feat_tiles = (n_feat + BF - 1) / BF;
     q.table = tl.table;
     q.stable = tl.stable;
     q.table_count = tl.count;
     q.out = out;
-    return launch_expert<T, 1, kEpiStore, BT, BF, STAGES, RB>(q, tl.cap * q.feat_tiles,
-                                                              max_small * q.feat_tiles, s);
+    return launch_expert<T, 1, kEpiStore, BT, BF, STAGES, RB, true>(q, tl.cap * q.feat_tiles,
+                                                                    max_small * q.feat_tiles, s);
 }
 
 // The up product with both results stored: a = act.W1[e]^T, g = act.W3[e]^T (rows gathered
@@ -1015,12 +1096,13 @@ hipError_t launch_grouped_gemm_gather(int dt, int N, int E, int H, int F, const 
                    : grouped_t<bf16_t>(N, E, H, F, x, token_ids, T, offsets, w1, w3, w2, h, y, a, g, ws, tables_ready, s);
 }
 
-hipError_t launch_grouped_nt(int dt, int N, int E, int K, int n_feat, const void* act,
-                             const int32_t* offsets, const void* w, long long w_stride,
-                             void* out, void* ws, hipStream_t s) {
+hipError_t launch_grouped_kmajor(int dt, int N, int E, int K, int n_feat, const void* act,
+                                 const int32_t* offsets, const void* w_lo, const void* w_hi,
+                                 int k_split, long long w_ld, long long w_stride, void* out,
+                                 void* ws, hipStream_t s) {
     if (N == 0) return hipSuccess;
-    return dt == 0 ? grouped_nt_t<float>(N, E, K, n_feat, act, offsets, w, w_stride, out, ws, s)
-                   : grouped_nt_t<bf16_t>(N, E, K, n_feat, act, offsets, w, w_stride, out, ws, s);
+    return dt == 0 ? grouped_kmajor_t<float>(N, E, K, n_feat, act, offsets, w_lo, w_hi, k_split, w_ld, w_stride, out, ws, s)
+                   : grouped_kmajor_t<bf16_t>(N, E, K, n_feat, act, offsets, w_lo, w_hi, k_split, w_ld, w_stride, out, ws, s);
 }
 
 hipError_t launch_grouped_pair(int dt, int N, int E, int H, int F, const void* act,

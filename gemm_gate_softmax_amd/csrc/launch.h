@@ -80,11 +80,14 @@ hipError_t launch_grouped_gemm_gather(int dt, int N, int E, int H, int F, const 
                                       void* g = nullptr, bool tables_ready = false);
 
 // ---- backward ----
-// out[p][f] = sum_k act[p][k] * w[e][f][k] over the expert segments (w advances w_stride
-// elements per expert); ws as for launch_grouped_gemm.
-hipError_t launch_grouped_nt(int dt, int N, int E, int K, int n_feat, const void* act,
-                             const int32_t* offsets, const void* w, long long w_stride,
-                             void* out, void* ws, hipStream_t s);
+// out[p][n] = sum_k act[p][k] * W_e[k][n] over the expert segments, with W_e's row k the
+// row k of w_lo[e] below k_split and row k - k_split of w_hi[e] (nullable) from there on;
+// rows w_ld elements apart, experts w_stride apart (k_split a multiple of 64, n_feat of 64).
+// ws as for launch_grouped_gemm.
+hipError_t launch_grouped_kmajor(int dt, int N, int E, int K, int n_feat, const void* act,
+                                 const int32_t* offsets, const void* w_lo, const void* w_hi,
+                                 int k_split, long long w_ld, long long w_stride, void* out,
+                                 void* ws, hipStream_t s);
 // a = act.W1[e]^T and g = act.W3[e]^T, [N][F] each (act rows through gather when not NULL).
 hipError_t launch_grouped_pair(int dt, int N, int E, int H, int F, const void* act,
                                const int32_t* gather, int src_rows, const int32_t* offsets,
