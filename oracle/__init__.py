@@ -39,11 +39,16 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
+    """The compiled oracle.  ``ORACLE_LIB`` names a separately compiled copy to load instead
+    (the mutation tests point it at deliberately broken builds of this source)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("ORACLE_LIB")
+        if path is None:
+            path = _LIB
+            if not os.path.exists(path):
+                build()
+        L = ctypes.CDLL(path)
         vp, i32, lng = ctypes.c_void_p, ctypes.c_int, ctypes.c_long
         L.oracle_gate_topk.argtypes = [i32] * 6 + [vp] * 7
         L.oracle_pft_build.argtypes = [i32] * 3 + [vp] * 6
