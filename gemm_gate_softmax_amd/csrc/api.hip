@@ -221,7 +221,7 @@ moe_status_t run_layer_forward(moe_dtype_t dt, int T, int H, int E, int F, int k
     const bool fast = moe::pft_layer_fast(T, E);
     int* hist = fast ? moe::pft_layer_hist(ws_pft, T, k) : nullptr;
     const int hist_n = fast ? ((T + moe::kPftSegTokens - 1) / moe::kPftSegTokens) * E : 0;
-    const moe::TileTables tables = moe::gemm_tables(ws_gemm, N, E);
+    const moe::TileTables tables = moe::gemm_tables(ws_gemm, N, E, F);
     MOE_TRY(launched(moe::launch_gate_logits(dt, T, H, E, x, wg, partials, refined, hist, hist_n,
                                              s)));
     MOE_TRY(launched(moe::launch_topk(dt, T, E, k, routing, moe::gate_splits(dt, T, H, E),

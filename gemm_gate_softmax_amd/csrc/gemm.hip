@@ -813,15 +813,22 @@ __host__ __device__ inline long long tiles_cap(long long N, int E, int btok = kE
     return (N + btok - 1) / btok + (E < N ? E : N);
 }
 
-// Small problems: below kSmallProblemRows routed rows the forward's expert products use
-// 64-token tiles with narrower feature tiles (up 64 features per operand, down 128), so
-// the few tiles there are spread over 4 to 8 times as many SIMDs.  A 128-token tile runs
-// its MFMAs one after another on four SIMDs; with fp32 (4096 flop per 64-cycle MFMA) a
-// 128 x 256 x 256 tile alone takes about 30 us, which set the Tiny layer's time.
-constexpr int kSmallProblemRows = 8192;
+// Small problems: when the usual tiles would not give every CU one (an upper bound on the
+// up product's 128-token tiles, (ceil(N / 128) + min(E, N)) x ceil(F / 128), below the 256
+// CUs), the forward's expert products use 64-token tiles with narrower feature tiles (up 64
+// features per operand, down 128), so the few tiles there are spread over 4 to 8 times as
+// many SIMDs.  A 128-token tile runs its MFMAs one after another on four SIMDs; with fp32
+// (4096 flop per 64-cycle MFMA) a 128 x 256 x 256 tile alone takes about 30 us, which set
+// the Tiny layer's time.  (A row-count threshold of 8192 also sent a dense 4096 x 7168 x
+// 2048 up product to the small tiles: 335 us against 224 us on the usual ones.)
+constexpr int kSmallProblemTiles = 256;
 constexpr int kSmallProblemBTok = 64;
 
-inline int fwd_btok(long long N) { return N < kSmallProblemRows ? kSmallProblemBTok : kExpertBTok; }
+inline int fwd_btok(long long N, int E, int F) {
+    const long long tiles = ((N + kExpertBTok - 1) / kExpertBTok + (E < N ? E : N)) *
+                            ((F + kExpertUpBF - 1) / kExpertUpBF);
+    return tiles < kSmallProblemTiles ? kSmallProblemBTok : kExpertBTok;
+}
 
 inline TileTables carve_tables(void* ws, long long N, int E, int btok = kExpertBTok) {
     TileTables t;
@@ -853,7 +860,7 @@ hipError_t grouped_t(int N, int E, int H, int F, const void* xd, const int32_t* 
                      int src_rows, const int32_t* offsets, const void* w1, const void* w3,
                      const void* w2, void* h, void* y, void* a, void* g, void* ws,
                      bool tables_ready, hipStream_t s) {
-    const TileTables tl = carve_tables(ws, N, E, fwd_btok(N));
+    const TileTables tl = carve_tables(ws, N, E, fwd_btok(N, E, F));
     hipError_t err = tables_ready ? hipSuccess : build_tables(tl, offsets, E, N, s);
     if (err != hipSuccess) return err;
     if (tl.btok == kSmallProblemBTok)
@@ -1063,7 +1070,9 @@ size_t gemm_ws_bytes(long long N, int E) {
     return 256 + (size_t)(tiles_cap(N, E, kSmallProblemBTok) + E) * sizeof(int4);
 }
 
-TileTables gemm_tables(void* ws, long long N, int E) { return carve_tables(ws, N, E, fwd_btok(N)); }
+TileTables gemm_tables(void* ws, long long N, int E, int F) {
+    return carve_tables(ws, N, E, fwd_btok(N, E, F));
+}
 
 int gate_splits(int dt, int T, int H, int E) {
     const int nk = H * (dt == 0 ? 4 : 2) / kGateRB;

@@ -22,7 +22,7 @@ struct TileTables {
     int btok;
     int small;
 };
-TileTables gemm_tables(void* ws, long long N, int E);
+TileTables gemm_tables(void* ws, long long N, int E, int F);
 
 // Gate logits x.Wg^T as gate_splits() fp32 partial sums over K splits, [split][T][E] in
 // `partials` (no bias).  *zero_word (may be NULL) and zero_buf[0, zero_n) are set to 0 by

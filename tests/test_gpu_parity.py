@@ -272,8 +272,8 @@ def test_grouped_gemm_parity(orc, dt, N, E, H, F):
 def test_grouped_gemm_tile_boundaries(orc, dt, pad):
     """Segments on both sides of every tile-size boundary: experts of up to 64 rows take
     one 64-token tile, larger ones 128-token tiles with a ragged last tile (64-token tiles
-    below 8192 rows in all: pad adds an expert that lifts the call over that line); empty
-    experts take none."""
+    when the call has fewer 128-token tiles than CUs: pad adds an expert that lifts it over
+    that line); empty experts take none."""
     counts = [64, 65, 1, 0, 63, 128, 129, 0, 192, 64, 2, 255, 256, 257, 0, 33] + ([pad] if pad else [])
     E, H, F = len(counts), 128, 320
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
