@@ -12,10 +12,11 @@
 //   gate:     dl from dw through the routing weights of the picked logits (softmax over the
 //             picks, or normalised sigmoids), dx[t] += sum_j dl_j Wg[e_j],
 //             dWg = DL^T x, dbias = column sums of DL (DL [T][E] holds dl at the picks)
-// Every product runs on the tile GEMM of gemm.hip: dh and dxd read the stored weights
-// K-major (transposed in the LDS fragment read), and the weight gradients read activations
-// transposed into per-expert column blocks aligned to 64 and zero padded, so each expert's
-// gradient is one GEMM over its own K range.  All accumulation is fp32; every gradient tensor is rounded once to its storage
+// Every product runs on the tile GEMM of gemm.hip, reading its operands as stored: dh and
+// dxd take the weights K-major, and each expert's weight gradient is one GEMM over its own
+// rows with both row-major operands read K-major (the transpose happens in the LDS
+// fragment read; the last k-slice reads zeros past the expert's rows).  Only dWg reads x
+// and the logit gradients transposed into a column block.  All accumulation is fp32; every gradient tensor is rounded once to its storage
 // type (dbias, dw and dl stay fp32).  Deterministic: no atomics.
 #include "device.h"
 #include "launch.h"
@@ -373,36 +374,6 @@ __global__ __launch_bounds__(1024) void split_experts_kernel(const int32_t* __re
     if (e == 1023) *nlist = scan[cur][e];
 }
 
-// kofs[e] = sum_{e' < e} round_up(counts[e'], 64); one workgroup of 1024 threads (E <= 1024).
-__global__ __launch_bounds__(1024) void kofs_kernel(const int32_t* __restrict__ counts, int E,
-                                                    int32_t* __restrict__ kofs) {
-    __shared__ int scan[2][1024];
-    const int e = threadIdx.x;
-    const int v = e < E ? (counts[e] + kTile - 1) / kTile * kTile : 0;
-    int cur = 0;
-    scan[0][e] = v;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        const int s = scan[cur][e] + (e >= d ? scan[cur][e - d] : 0);
-        scan[cur ^ 1][e] = s;
-        cur ^= 1;
-        __syncthreads();
-    }
-    if (e < E) kofs[e] = scan[cur][e] - v;
-    if (e == E - 1) kofs[E] = scan[cur][e];
-}
-
-// pmap[q] = buffer row of column q (-1 in padding): block e < E covers expert e's block,
-// block E the tail [kofs[E], kmax).
-__global__ __launch_bounds__(256) void pmap_kernel(const int32_t* __restrict__ offsets,
-                                                   const int32_t* __restrict__ kofs, int E,
-                                                   int kmax, int32_t* __restrict__ pmap) {
-    const int e = blockIdx.x;
-    const int q0 = kofs[e], q1 = e < E ? kofs[e + 1] : kmax;
-    const int n = e < E ? offsets[e + 1] - offsets[e] : 0, base = e < E ? offsets[e] : 0;
-    for (int q = q0 + threadIdx.x; q < q1; q += 256) pmap[q] = q - q0 < n ? base + (q - q0) : -1;
-}
-
 template <typename T>
 hipError_t seg_transpose(const void* in, int C, const int32_t* gather, const int32_t* pmap, int R,
                          int kmax, void* out, hipStream_t s) {
@@ -416,10 +387,10 @@ size_t align_up(size_t v) { return (v + 255) / 256 * 256; }
 
 // Workspace layout of the layer backward (every piece 256-byte aligned).
 struct BwdWs {
-    void *gemm, *dy, *dh, *a, *g, *dag, *dxd, *dyt, *ht, *xdt, *dagt, *dlt, *xt;
+    void *gemm, *dy, *dh, *a, *g, *dag, *dxd, *xd, *dlt, *xt;
     float *dw, *dl;
-    int32_t *kofs, *pmap, *gofs, *elist, *nlist;
-    int kmax, tpad;
+    int32_t *gofs, *elist, *nlist, *zero;
+    int tpad;
     size_t bytes;
 };
 
@@ -427,7 +398,6 @@ BwdWs carve_bwd(void* base, int dt, int T, int H, int E, int F, int k) {
     const size_t es = dt == 0 ? 4 : 2;
     const long long N = (long long)T * k;
     BwdWs w{};
-    w.kmax = (int)((N + kTile - 1) / kTile * kTile + (long long)kTile * E);
     w.tpad = (T + kTile - 1) / kTile * kTile;
     char* p = static_cast<char*>(base);
     size_t off = 0;
@@ -443,24 +413,23 @@ BwdWs carve_bwd(void* base, int dt, int T, int H, int E, int F, int k) {
     w.g = take(es * N * F);
     w.dag = take(es * N * 2 * F);
     w.dxd = take(es * N * H);
-    w.dyt = take(es * H * w.kmax);
-    w.ht = take(es * F * w.kmax);
-    w.xdt = take(es * H * w.kmax);
-    w.dagt = take(es * 2 * F * w.kmax);
+    w.xd = take(es * N * H);          // the dispatched rows, when the forward gathered them
     w.dlt = take(es * E * w.tpad);
     w.xt = take(es * H * w.tpad);
     w.dw = static_cast<float*>(take(4 * N));
     w.dl = static_cast<float*>(take(4 * N));
-    w.kofs = static_cast<int32_t*>(take(4 * (E + 1)));
-    w.pmap = static_cast<int32_t*>(take(4 * (size_t)w.kmax));
     w.gofs = static_cast<int32_t*>(take(8));
+    w.zero = static_cast<int32_t*>(take(64));
     w.elist = static_cast<int32_t*>(take(4 * (size_t)E));
     w.nlist = static_cast<int32_t*>(take(4));
     w.bytes = off;
     return w;
 }
 
-__global__ void set_gofs_kernel(int32_t* gofs, int tpad) {
+// The gate gradient's one column block [0, tpad) and 64 zero bytes (what the weight
+// gradients' last k-slice reads past an expert's rows).
+__global__ void set_gofs_kernel(int32_t* gofs, int tpad, int32_t* zero) {
+    if (threadIdx.x < 16) zero[threadIdx.x] = 0;
     if (threadIdx.x == 0) {
         gofs[0] = 0;
         gofs[1] = tpad;
@@ -505,15 +474,14 @@ hipError_t layer_backward_t(const BwdParams& b, hipStream_t s) {
     MOE_CHECK(hipGetLastError());
     MOE_CHECK(launch_grouped_kmajor(dt, N, E, 2 * F, H, w.dag, b.offsets, b.w1, b.w3, F, H,
                                     (long long)F * H, w.dxd, w.gemm, s));
-    // per-expert column blocks for the weight gradients
-    hipLaunchKernelGGL(kofs_kernel, dim3(1), dim3(1024), 0, s, b.counts, E, w.kofs);
+    // the dispatched rows for the weight gradients (the forward gathered them from x)
+    const void* xd_rows = b.xd;
+    if (!b.xd) {
+        MOE_CHECK(launch_dispatch(dt, T_, k, H, b.x, b.dest_pos, w.xd, s));
+        xd_rows = w.xd;
+    }
+    hipLaunchKernelGGL(set_gofs_kernel, dim3(1), dim3(64), 0, s, w.gofs, w.tpad, w.zero);
     MOE_CHECK(hipGetLastError());
-    hipLaunchKernelGGL(pmap_kernel, dim3(E + 1), dim3(256), 0, s, b.offsets, w.kofs, E, w.kmax, w.pmap);
-    MOE_CHECK(hipGetLastError());
-    MOE_CHECK(seg_transpose<T>(w.dy, H, nullptr, w.pmap, N, w.kmax, w.dyt, s));
-    MOE_CHECK(seg_transpose<T>(b.h, F, nullptr, w.pmap, N, w.kmax, w.ht, s));
-    MOE_CHECK(seg_transpose<T>(act, H, gather, w.pmap, N, w.kmax, w.xdt, s));
-    MOE_CHECK(seg_transpose<T>(w.dag, 2 * F, nullptr, w.pmap, N, w.kmax, w.dagt, s));
     // weight gradients: experts with at most kOuterRows rows (or none) as outer products,
     // the others on the tile GEMM over their column blocks
     hipLaunchKernelGGL(split_experts_kernel, dim3(1), dim3(1024), 0, s, b.counts, E, kOuterRows,
@@ -529,11 +497,14 @@ hipError_t layer_backward_t(const BwdParams& b, hipStream_t s) {
                            gather, b.offsets, F, H, static_cast<T*>(half ? b.dw3 : b.dw1));
         MOE_CHECK(hipGetLastError());
     }
+    // the listed experts' gradients from the row-major buffers, read K-major
     const size_t es = sizeof(T);
-    MOE_CHECK(launch_wgrad(dt, E, H, F, w.kmax, w.dyt, w.ht, w.kofs, w.elist, w.nlist, b.dw2, s));
-    MOE_CHECK(launch_wgrad(dt, E, F, H, w.kmax, w.dagt, w.xdt, w.kofs, w.elist, w.nlist, b.dw1, s));
-    MOE_CHECK(launch_wgrad(dt, E, F, H, w.kmax, static_cast<const char*>(w.dagt) + es * F * w.kmax,
-                           w.xdt, w.kofs, w.elist, w.nlist, b.dw3, s));
+    MOE_CHECK(launch_wgrad_rows(dt, E, H, F, w.dy, H, b.h, F, b.offsets, w.elist, w.nlist, w.zero,
+                                b.dw2, s));
+    MOE_CHECK(launch_wgrad_rows(dt, E, F, H, w.dag, 2 * F, xd_rows, H, b.offsets, w.elist, w.nlist,
+                                w.zero, b.dw1, s));
+    MOE_CHECK(launch_wgrad_rows(dt, E, F, H, static_cast<const char*>(w.dag) + es * F, 2 * F, xd_rows,
+                                H, b.offsets, w.elist, w.nlist, w.zero, b.dw3, s));
     // gate: dl, then dx (dispatch backward + gate), dWg and dbias
     hipLaunchKernelGGL(gate_dl_kernel<T>, dim3((T_ + 3) / 4), dim3(256), 0, s,
                        static_cast<const uint4*>(b.x), static_cast<const uint4*>(b.wg), b.bias,
@@ -548,8 +519,6 @@ hipError_t layer_backward_t(const BwdParams& b, hipStream_t s) {
                        b.top_experts, T_, E, k, w.tpad, static_cast<T*>(w.dlt));
     MOE_CHECK(hipGetLastError());
     MOE_CHECK(seg_transpose<T>(b.x, H, nullptr, nullptr, T_, w.tpad, w.xt, s));
-    hipLaunchKernelGGL(set_gofs_kernel, dim3(1), dim3(64), 0, s, w.gofs, w.tpad);
-    MOE_CHECK(hipGetLastError());
     MOE_CHECK(launch_wgrad(dt, 1, E, H, w.tpad, w.dlt, w.xt, w.gofs, nullptr, nullptr, b.dwg, s));
     hipLaunchKernelGGL(gate_dbias_kernel, dim3(E), dim3(256), 0, s, w.dl, b.offsets, b.token_ids,
                        b.dest_pos, k, b.dbias);

@@ -126,6 +126,10 @@ struct GemmParams {
     long long w_ld;         // K-major weights: elements from one k row to the next
     int w_k2;               // K-major weights: first k-slice read from the second tensor
     long long w_k2_adj;     // bytes added to weight addresses from k-slice w_k2 on
+    long long a_ld;         // K-major activations: elements from one k row to the next
+    int k_rows;             // K-major operands: k rows of the tile's K range (rows past it
+                            // are read from zero16)
+    const void* zero16;     // 16 zero bytes
     int* zero_word;         // dense product: set to 0 by workgroup 0 (nullable)
     int* zero_buf;          // dense product: zero_buf[0, zero_n) set to 0 (nullable)
     int zero_n;
@@ -283,9 +287,11 @@ __device__ __forceinline__ uint4 kmajor_frag(const char* region, int mrow, int k
 // read while stage kt+S-1 is loaded into the slot stage kt-1 left.  WNT marks the weight
 // transfers non-temporal: for a tile that is the only reader of its weights.  The tile
 // visits k-slices rot, rot+1, ..., nk-1, 0, ..., rot-1 of its K range (rot < nk).  WKM:
-// the weights are stored K-major (w[b][k][n], rows w_ld apart), see kmajor_frag.
+// the weights are stored K-major (w[b][k][n], rows w_ld apart), see kmajor_frag; AKM: the
+// activations too (act[k][m], rows a_ld apart; the tile's "rows" are then m).  K-major
+// rows at or past k_rows read zeros.
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool FULL, bool WNT = false,
-          bool WKM = false>
+          bool WKM = false, bool AKM = false>
 __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* lds, int expert,
                                              int row0, int row_end, int f0, int s0, int nk,
                                              int rot = 0) {
@@ -314,25 +320,35 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
         // (4 kRowsPerDma i - BT) / BF: both compile-time once i is unrolled. ----
         const int lw = wave - 4;
         constexpr int kBlkRows = 4 * kRowsPerDma;                     // rows per i step
+        constexpr int KPS = kRowBytes / (int)sizeof(T), kPer = 16 / (int)sizeof(T);
         const char* src[kDma];
+        int krow[kDma];                                               // K-major: k row held
 #pragma unroll
         for (int i = 0; i < kDma; ++i) {
             const int rl = lane / kChunks;                            // row within the block
             const int r = (lw + 4 * i) * kRowsPerDma + rl;            // row within the stage
             const int c = (lane % kChunks) ^ chunk_swizzle<RB>(r);    // chunk held by this slot
-            if (i < BT / kBlkRows) {
+            krow[i] = 0;
+            if (i < BT / kBlkRows && AKM) {
+                // k row kr of n-block nb of the activations (n = m); this slot holds chunk cw
+                const int nb = r / KPS, kr = r % KPS;
+                const int cw = (lane % kChunks) ^ kmajor_swizzle(kr);
+                const int m = min(row0 + nb * KPS + cw * kPer, p.act_rows - kPer);
+                src[i] = reinterpret_cast<const char*>(p.act + ((size_t)s0 * KPS + kr) * p.a_ld + m);
+                krow[i] = kr;
+            } else if (i < BT / kBlkRows) {
                 int ar = min(row0 + r, p.act_rows - 1);
                 if (p.gather) ar = min(max(p.gather[ar], 0), p.src_rows - 1);   // fused dispatch
                 src[i] = reinterpret_cast<const char*>(p.act) + (size_t)ar * row_bytes + k_off + c * 16;
             } else if constexpr (WKM) {
                 // k row kr of n-block nb of operand b; this slot holds its chunk cw
-                constexpr int KPS = kRowBytes / (int)sizeof(T), kPer = 16 / (int)sizeof(T);
                 const int b = (kBlkRows * i - BT) / BF;
                 const int rr = r - BT - b * BF, nb = rr / KPS, kr = rr % KPS;
                 const int cw = (lane % kChunks) ^ kmajor_swizzle(kr);
                 const int n = min(f0 + nb * KPS + cw * kPer, p.n_feat - kPer);
                 src[i] = reinterpret_cast<const char*>(p.w[b] + (size_t)expert * p.w_stride +
                                                        ((size_t)s0 * KPS + kr) * p.w_ld + n);
+                krow[i] = kr;
             } else {
                 const int b = (kBlkRows * i - BT) / BF;
                 const int f = min(f0 + (r - BT) - b * BF, p.n_feat - 1);
@@ -351,12 +367,14 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
         // skipped rows' LDS holds stale data that only ever meets the MFMA columns of
         // tokens that are never stored.
         constexpr int kActDma = BT / kBlkRows;                         // activation blocks per loader
-        const int nact = FULL ? kActDma
-                              : min(max((min(row_end - row0, BT) - lw * kRowsPerDma + kBlkRows - 1) /
-                                            kBlkRows, 0), kActDma);
+        const int nact = FULL || AKM ? kActDma
+                                     : min(max((min(row_end - row0, BT) - lw * kRowsPerDma + kBlkRows - 1) /
+                                                   kBlkRows, 0), kActDma);
         const int keff = kDma - (kActDma - nact);                     // transfers per slice
         // K-major weights advance by KPS rows per k-slice (and switch tensors at w_k2)
-        const long long wslice = WKM ? (long long)(kRowBytes / (int)sizeof(T)) * p.w_ld * (long long)sizeof(T) : 0;
+        const long long wslice = WKM ? (long long)KPS * p.w_ld * (long long)sizeof(T) : 0;
+        const long long aslice = AKM ? (long long)KPS * p.a_ld * (long long)sizeof(T) : 0;
+        const char* zero16 = static_cast<const char*>(p.zero16);
 #define MOE_ISSUE(KT, SLOT)                                                                   \
         do {                                                                                 \
             const uint32_t b_ = __builtin_amdgcn_readfirstlane(wbase + (SLOT) * kStageBytes); \
@@ -364,10 +382,14 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
             const int kk_ = ks_ >= nk ? ks_ - nk : ks_;                                      \
             const size_t o_ = (size_t)kk_ * kRowBytes;                                       \
             const long long ow_ = WKM ? kk_ * wslice + (kk_ >= p.w_k2 ? p.w_k2_adj : 0) : (long long)o_; \
-            _Pragma("unroll") for (int i_ = 0; i_ < kDma; ++i_)                              \
-                if (i_ >= kActDma && WNT) dma16_nt(src[i_] + ow_, b_ + i_ * 4096);          \
-                else if (i_ >= kActDma) dma16(src[i_] + ow_, b_ + i_ * 4096);               \
-                else if (i_ < nact) dma16(src[i_] + o_, b_ + i_ * 4096);                    \
+            const long long oa_ = AKM ? kk_ * aslice : (long long)o_;                       \
+            _Pragma("unroll") for (int i_ = 0; i_ < kDma; ++i_) {                            \
+                const bool w_ = i_ >= kActDma;                                               \
+                const char* a_ = src[i_] + (w_ ? ow_ : oa_);                                 \
+                if ((w_ ? WKM : AKM) && kk_ * KPS + krow[i_] >= p.k_rows) a_ = zero16;       \
+                if (w_ && WNT) dma16_nt(a_, b_ + i_ * 4096);                                 \
+                else if (w_ || i_ < nact) dma16(a_, b_ + i_ * 4096);                         \
+            }                                                                                \
         } while (0)
         if (nk == 1) {
             // a single k-slice (weight gradients of experts with at most 64 rows): no
@@ -431,8 +453,11 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
     do {                                                                                     \
         const char* st_ = (STAGE);                                                           \
         const int cs_ = ((2 * (KSTEP) + lhalf) ^ swz) * 16;                                  \
-        _Pragma("unroll") for (int j = 0; j < TT; ++j) FA[j] =                               \
-            *reinterpret_cast<const uint4*>(st_ + (wt * (BT / 2) + j * 32 + l32) * kRowBytes + cs_); \
+        _Pragma("unroll") for (int j = 0; j < TT; ++j) {                                     \
+            if constexpr (AKM) FA[j] = kmajor_frag<T, RB>(st_, wt * (BT / 2) + j * 32, (KSTEP), lane); \
+            else FA[j] = *reinterpret_cast<const uint4*>(                                    \
+                st_ + (wt * (BT / 2) + j * 32 + l32) * kRowBytes + cs_);                     \
+        }                                                                                    \
         _Pragma("unroll") for (int b = 0; b < NB; ++b)                                       \
             _Pragma("unroll") for (int i = 0; i < FT; ++i) {                                 \
                 if constexpr (WKM) FW[b][i] = kmajor_frag<T, RB>(st_ + (BT + b * BF) * kRowBytes, \
@@ -944,6 +969,7 @@ hipError_t grouped_kmajor_t(int N, int E, int K, int n_feat, const void* act,
     q.w[0] = static_cast<const T*>(w_lo);
     q.w_stride = w_stride;
     q.w_ld = w_ld;
+    q.k_rows = K;                // every row of the K range exists: nothing reads zero16
     q.w_k2 = 1 << 30;
     if (w_hi != nullptr) {
         // from k-slice w_k2 on, addresses computed from w_lo land in w_hi
@@ -994,12 +1020,15 @@ hipError_t grouped_pair_t(int N, int E, int H, int F, const void* act, const int
                                                              max_small * q.feat_tiles, s);
 }
 
-// Weight gradients: out[e][m][f] = sum over k in [kofs[e], kofs[e+1]) of act[m][k] * w[f][k].
-// act [M][Ktot] and w [n_feat][Ktot] hold every expert's rows as a column block starting at
+// Weight gradients, out[e][m][f] = sum over expert e's rows k of act[k][m] * w[k][f], in two
+// layouts.  KM: act [N][a_ld] and w [N][w_ld] as the forward and backward wrote them (row k
+// of expert e in [kofs[e], kofs[e+1]), here the expert offsets), both read K-major; the
+// last k-slice's rows past the expert's end read zeros.  Otherwise act [M][Ktot] and
+// w [n_feat][Ktot] hold every expert's rows transposed into a column block starting at
 // kofs[e] (a multiple of 64, zero padded to a multiple of 64).  Work item (expert, m tile,
-// f tile) over every expert or over the experts listed in elist[0, *nlist);
-// an expert with no rows gets a zero gradient.
-template <typename T, int BT, int BF, int S, int RB>
+// f tile) over every expert or over the experts listed in elist[0, *nlist); an expert with
+// no rows gets a zero gradient.
+template <typename T, int BT, int BF, int S, int RB, bool KM>
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(GemmParams<T, 1> p,
                                                             const int32_t* kofs, int E, int M,
                                                             const int32_t* elist,
@@ -1022,7 +1051,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(GemmParams<T, 1> p,
     GemmParams<T, 1> q = p;
     q.out = static_cast<T*>(p.out) + (size_t)e * M * p.n_feat;
     const int k0 = kofs[e], k1 = kofs[e + 1];
-    const int nk = (int)((size_t)(k1 - k0) * sizeof(T) / RB);
+    constexpr int KPS = RB / (int)sizeof(T);
+    const int nk = KM ? (k1 - k0 + KPS - 1) / KPS : (int)((size_t)(k1 - k0) * sizeof(T) / RB);
     const int row0 = mt * BT;
     if (nk <= 0) {                                  // whole workgroup: no barrier is pending
         constexpr int kPer = 16 / (int)sizeof(T);
@@ -1034,11 +1064,21 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(GemmParams<T, 1> p,
         }
         return;
     }
-    const int s0 = (int)((size_t)k0 * sizeof(T) / RB);
-    if (row0 + BT <= M)
-        compute_tile<T, 1, kEpiStore, BT, BF, S, RB, true>(q, lds, 0, row0, M, ft * BF, s0, nk);
-    else
-        compute_tile<T, 1, kEpiStore, BT, BF, S, RB, false>(q, lds, 0, row0, M, ft * BF, s0, nk);
+    if constexpr (KM) {
+        q.act = p.act + (size_t)k0 * p.a_ld;
+        q.w[0] = p.w[0] + (size_t)k0 * p.w_ld;
+        q.k_rows = k1 - k0;
+        if (row0 + BT <= M)
+            compute_tile<T, 1, kEpiStore, BT, BF, S, RB, true, false, true, true>(q, lds, 0, row0, M, ft * BF, 0, nk);
+        else
+            compute_tile<T, 1, kEpiStore, BT, BF, S, RB, false, false, true, true>(q, lds, 0, row0, M, ft * BF, 0, nk);
+    } else {
+        const int s0 = (int)((size_t)k0 * sizeof(T) / RB);
+        if (row0 + BT <= M)
+            compute_tile<T, 1, kEpiStore, BT, BF, S, RB, true>(q, lds, 0, row0, M, ft * BF, s0, nk);
+        else
+            compute_tile<T, 1, kEpiStore, BT, BF, S, RB, false>(q, lds, 0, row0, M, ft * BF, s0, nk);
+    }
 }
 
 template <typename T>
@@ -1059,8 +1099,33 @@ hipError_t wgrad_t(int E, int M, int n_feat, int ktot, const void* act, const vo
     const long long per_x = ((long long)((M + BT - 1) / BT) * q.feat_tiles + 7) / 8;
     const long long grid = 8 * per_x * E;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((wgrad_kernel<T, BT, BF, STAGES, RB>), dim3((unsigned)grid), dim3(kThreads),
+    hipLaunchKernelGGL((wgrad_kernel<T, BT, BF, STAGES, RB, false>), dim3((unsigned)grid), dim3(kThreads),
                        0, s, q, kofs, E, M, elist, nlist);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t wgrad_rows_t(int E, int M, int n_feat, const void* act, long long a_ld, const void* w,
+                        long long w_ld, const int32_t* offsets, const int32_t* elist,
+                        const int32_t* nlist, const void* zero16, void* out, hipStream_t s) {
+    constexpr int BT = kExpertBTok, BF = kExpertDownBF, STAGES = kExpertStages,
+                  RB = kExpertRowBytes;
+    GemmParams<T, 1> q{};
+    q.act = static_cast<const T*>(act);
+    q.act_rows = M;
+    q.a_ld = a_ld;
+    q.w[0] = static_cast<const T*>(w);
+    q.w_ld = w_ld;
+    q.w_k2 = 1 << 30;
+    q.zero16 = zero16;
+    q.n_feat = n_feat;
+    q.feat_tiles = (n_feat + BF - 1) / BF;
+    q.out = out;
+    const long long per_x = ((long long)((M + BT - 1) / BT) * q.feat_tiles + 7) / 8;
+    const long long grid = 8 * per_x * E;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((wgrad_kernel<T, BT, BF, STAGES, RB, true>), dim3((unsigned)grid), dim3(kThreads),
+                       0, s, q, offsets, E, M, elist, nlist);
     return hipGetLastError();
 }
 
@@ -1123,6 +1188,14 @@ hipError_t launch_grouped_pair(int dt, int N, int E, int H, int F, const void* a
     if (N == 0) return hipSuccess;
     return dt == 0 ? grouped_pair_t<float>(N, E, H, F, act, gather, src_rows, offsets, w1, w3, a, g, ws, s)
                    : grouped_pair_t<bf16_t>(N, E, H, F, act, gather, src_rows, offsets, w1, w3, a, g, ws, s);
+}
+
+hipError_t launch_wgrad_rows(int dt, int E, int M, int n_feat, const void* act, long long a_ld,
+                             const void* w, long long w_ld, const int32_t* offsets,
+                             const int32_t* elist, const int32_t* nlist, const void* zero16,
+                             void* out, hipStream_t s) {
+    return dt == 0 ? wgrad_rows_t<float>(E, M, n_feat, act, a_ld, w, w_ld, offsets, elist, nlist, zero16, out, s)
+                   : wgrad_rows_t<bf16_t>(E, M, n_feat, act, a_ld, w, w_ld, offsets, elist, nlist, zero16, out, s);
 }
 
 hipError_t launch_wgrad(int dt, int E, int M, int n_feat, int ktot, const void* act,

@@ -93,6 +93,14 @@ hipError_t launch_grouped_pair(int dt, int N, int E, int H, int F, const void* a
                                const int32_t* gather, int src_rows, const int32_t* offsets,
                                const void* w1, const void* w3, void* a, void* g, void* ws,
                                hipStream_t s);
+// out[e][m][f] = sum over the rows k of expert e (offsets) of act[k][m] * w[k][f], act and w
+// row-major with rows a_ld and w_ld elements apart (act may start at a column offset), for
+// the experts listed in elist[0, *nlist) (E an upper bound of *nlist); M and n_feat
+// multiples of 64; zero16: 16 zero bytes of device memory.
+hipError_t launch_wgrad_rows(int dt, int E, int M, int n_feat, const void* act, long long a_ld,
+                             const void* w, long long w_ld, const int32_t* offsets,
+                             const int32_t* elist, const int32_t* nlist, const void* zero16,
+                             void* out, hipStream_t s);
 // out[e][m][f] = sum_{k in [kofs[e], kofs[e+1])} act[m][k] * w[f][k]; act [M][ktot],
 // w [n_feat][ktot], kofs multiples of 64.  With elist (device, may be NULL) only the experts
 // elist[0, *nlist) are computed, E being an upper bound of *nlist.

@@ -254,11 +254,10 @@ moe_status_t moe_layer_forward_noalloc(moe_dtype_t dt, int T, int H, int E, int 
  * [E][F][H], dw2 [E][H][F] in the storage type; dbias [E] fp32; dtop_weights [T][k] fp32
  * (may be NULL).  Experts without rows get zero weight gradients.  All accumulation is
  * fp32, each output is rounded once; results are deterministic (no atomics).
- * ws: moe_workspace_bytes(MOE_WS_BACKWARD, ...) bytes: row-sized intermediates and the
- * activations transposed into per-expert column blocks, at most (4H + 8F)(Tk + 64E) +
- * (H + E)(T + 63) elements plus small tables (3.7 GB at T=4096, H=7168, E=256, F=2048, k=8,
- * bf16); the weights are read as stored, never copied.  T == 0 is a no-op (nothing is
- * written).
+ * ws: moe_workspace_bytes(MOE_WS_BACKWARD, ...) bytes: row-sized intermediates, about
+ * (3H + 5F)Tk + (H + E)(T + 63) elements plus small tables (2.1 GB at T=4096, H=7168,
+ * E=256, F=2048, k=8, bf16); the weights and the row-major activations are read as stored,
+ * never transposed into copies.  T == 0 is a no-op (nothing is written).
  */
 moe_status_t moe_layer_backward(moe_dtype_t dt, int T, int H, int E, int F, int k,
                                 moe_routing_t routing, const void *x, const void *wg,

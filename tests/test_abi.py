@@ -205,6 +205,6 @@ def test_backward_workspace_size(L):
     # under 4 GB at T=4096, H=7168, E=256, F=2048, top-8, bf16
     T, H, E, F, k = 4096, 7168, 256, 2048, 8
     big = ws(4, T, H, E, F, k, 1)
-    assert (4 * H + 8 * F) * T * k * 2 < big <= ((4 * H + 8 * F) * (T * k + 64 * E) + (H + E) * (T + 63)) * 2 + (1 << 20)
-    assert big < 4e9
+    assert (3 * H + 5 * F) * T * k * 2 < big <= ((3 * H + 5 * F) * T * k + (H + E) * (T + 63)) * 2 + (4 << 20)
+    assert big < 2.5e9
     assert ws(4, 8, 64, 4, 100, 2, 1) == 0              # F not a multiple of 64
