@@ -40,6 +40,10 @@ CASES = [
     (W.LayerConfig("small_bf16", T=300, H=256, E=16, F=192, k=4, dtype="bf16",
                    bias=("zipf", 1.2)), "sigmoid"),
     (W.LayerConfig("one_expert_f32", T=96, H=128, E=1, F=128, k=1, dtype="f32"), "softmax"),
+    # every expert above 64 rows: all weight gradients on the tile GEMM reading the row-major
+    # operands, expert offsets not multiples of 64, ragged last k-slices
+    (W.LayerConfig("rows_f32", T=333, H=192, E=5, F=128, k=2, dtype="f32"), "softmax"),
+    (W.LayerConfig("rows_bf16", T=333, H=192, E=5, F=128, k=2, dtype="bf16"), "softmax"),
 ]
 
 
@@ -69,6 +73,9 @@ def test_layer_backward_parity(cfg, routing):
     bias = None if d["bias"] is None else W.to_host(d["bias"], None)
     te_ref, _ = oracle.gate_topk(cfg.dtype, h["x"], h["wg"], bias, cfg.k, routing=routing)
     assert np.array_equal(W.to_host(bufs["top_experts"], None), te_ref), "routing differs"
+    if cfg.name.startswith("rows_"):
+        counts = W.to_host(bufs["counts"], None)
+        assert counts.min() > 64 and any(int(o) % 64 for o in W.to_host(bufs["offsets"], None)), counts
     ref = oracle.layer_backward(cfg.dtype, h["x"], h["wg"], bias, h["w1"], h["w3"], h["w2"],
                                 cfg.k, dout_h, routing=routing)
     for n in GRADS:
