@@ -761,9 +761,13 @@ hipError_t launch_dense(const GemmParams<T, NB>& p, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The grid covers the most (token tile, feature tile) items the two lists can hold
+// together, max_items = tiles_cap x feature tiles: an expert adds at most one tile beyond
+// its rows / BT, whichever list it is in.  XCD x runs ceil(m / 8) + ceil(s / 8) items of
+// the m and s that exist, at most max_items / 8 + 2.
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool WKM = false>
-hipError_t launch_expert(const GemmParams<T, NB>& p, int max_m, int max_s, hipStream_t s) {
-    const int grid = 8 * ((max_m + 7) / 8 + (max_s + 7) / 8);
+hipError_t launch_expert(const GemmParams<T, NB>& p, int max_items, hipStream_t s) {
+    const int grid = 8 * ((max_items + 7) / 8 + 2);
     if (grid <= 0) return hipSuccess;
     hipLaunchKernelGGL((expert_gemm_kernel<T, NB, EPI, BT, BF, S, RB, WKM>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
@@ -900,7 +904,6 @@ template <typename T, int BT, int UP_BF, int DN_BF>
 hipError_t grouped_tiles(int N, int E, int H, int F, const void* xd, const int32_t* gather,
                          int src_rows, const TileTables& tl, const void* w1, const void* w3,
                          const void* w2, void* h, void* y, void* a, void* g, hipStream_t s) {
-    const int max_small = kSmallBTok > 0 ? (E < N ? E : N) : 0;
     hipError_t err = hipSuccess;
     constexpr int STAGES = kExpertStages, RB = kExpertRowBytes;
     GemmParams<T, 2> up{};
@@ -922,10 +925,10 @@ hipError_t grouped_tiles(int N, int E, int H, int F, const void* xd, const int32
     up.out3 = g;
     if (a != nullptr && g != nullptr)
         err = launch_expert<T, 2, kEpiSwiGLUPair, BT, UP_BF, STAGES, RB>(
-            up, tl.cap * up.feat_tiles, max_small * up.feat_tiles, s);
+            up, tl.cap * up.feat_tiles, s);
     else
         err = launch_expert<T, 2, kEpiSwiGLU, BT, UP_BF, STAGES, RB>(
-            up, tl.cap * up.feat_tiles, max_small * up.feat_tiles, s);
+            up, tl.cap * up.feat_tiles, s);
     if (err != hipSuccess || w2 == nullptr) return err;      // up product only
 
     GemmParams<T, 1> dn{};
@@ -942,7 +945,7 @@ hipError_t grouped_tiles(int N, int E, int H, int F, const void* xd, const int32
     dn.group_tok = kGroupTokDown;
     dn.out = y;
     return launch_expert<T, 1, kEpiStore, BT, DN_BF, STAGES, RB>(
-        dn, tl.cap * dn.feat_tiles, max_small * dn.feat_tiles, s);
+        dn, tl.cap * dn.feat_tiles, s);
 }
 
 // ---- backward products ----
@@ -961,7 +964,6 @@ hipError_t grouped_kmajor_t(int N, int E, int K, int n_feat, const void* act,
     const TileTables tl = carve_tables(ws, N, E);
     hipError_t err = build_tables(tl, offsets, E, N, s);
     if (err != hipSuccess) return err;
-    const int max_small = kSmallBTok > 0 ? (E < N ? E : N) : 0;
     GemmParams<T, 1> q{};
     q.act = static_cast<const T*>(act);
     q.act_rows = N;
@@ -984,8 +986,7 @@ hipError_t grouped_kmajor_t(int N, int E, int K, int n_feat, const void* act,
     q.stable = tl.stable;
     q.table_count = tl.count;
     q.out = out;
-    return launch_expert<T, 1, kEpiStore, BT, BF, STAGES, RB, true>(q, tl.cap * q.feat_tiles,
-                                                                    max_small * q.feat_tiles, s);
+    return launch_expert<T, 1, kEpiStore, BT, BF, STAGES, RB, true>(q, tl.cap * q.feat_tiles, s);
 }
 
 // The up product with both results stored: a = act.W1[e]^T, g = act.W3[e]^T (rows gathered
@@ -999,7 +1000,6 @@ hipError_t grouped_pair_t(int N, int E, int H, int F, const void* act, const int
     const TileTables tl = carve_tables(ws, N, E);
     hipError_t err = build_tables(tl, offsets, E, N, s);
     if (err != hipSuccess) return err;
-    const int max_small = kSmallBTok > 0 ? (E < N ? E : N) : 0;
     GemmParams<T, 2> q{};
     q.act = static_cast<const T*>(act);
     q.act_rows = N;
@@ -1016,8 +1016,7 @@ hipError_t grouped_pair_t(int N, int E, int H, int F, const void* act, const int
     q.table_count = tl.count;
     q.out = a;
     q.out2 = g;
-    return launch_expert<T, 2, kEpiPair, BT, BF, STAGES, RB>(q, tl.cap * q.feat_tiles,
-                                                             max_small * q.feat_tiles, s);
+    return launch_expert<T, 2, kEpiPair, BT, BF, STAGES, RB>(q, tl.cap * q.feat_tiles, s);
 }
 
 // Weight gradients, out[e][m][f] = sum over expert e's rows k of act[k][m] * w[k][f], in two
