@@ -7,12 +7,15 @@
 // end are computed from clamped addresses and never stored, and an expert with no rows
 // contributes no tile, so its weights are never read.
 //
-// Every product here is "NT": both operands are rows contiguous in the shared dimension
-// K (activations [rows][K], weights [features][K]).  NB = 2 fuses the SwiGLU gate and up
+// The forward's products are "NT": both operands are rows contiguous in the shared
+// dimension K (activations [rows][K], weights [features][K]).  The backward's products
+// also take operands stored K-major (weights [K][features], activations [K][rows]) as they
+// are, transposing them in the LDS fragment read.  NB = 2 fuses the SwiGLU gate and up
 // products so the epilogue forms silu(a) * g in registers.
 //
 // An expert tile is 128 tokens x (128 x NB or 256) features, or 64 tokens for an expert
-// with at most 64 rows.  A workgroup is 4 loader waves, which stage the operands through
+// with at most 64 rows (and for every expert of a problem too small to give each CU a
+// usual tile).  A workgroup is 4 loader waves, which stage the operands through
 // an LDS ring with direct-to-LDS transfers, and 4 compute waves in a 2 x 2 layout, which
 // read the ring and issue the MFMAs.  An expert with a handful of rows still gets a whole
 // tile (its MFMAs and activation transfers for empty token columns are skipped): its time
