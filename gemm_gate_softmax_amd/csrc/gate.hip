@@ -123,6 +123,7 @@ constexpr float kTieRel = MOE_TIE_REL;
 // The four waves of a block (one token each) share those dot products, a quarter of each
 // row per wave, summed in wave order; such tokens are counted in *refined.
 constexpr int kCandMax = 1024 + kWave;      // candidates of one token: at most E + 1
+constexpr int kMaxSplits = 8;               // K splits of the gate logits (gate_splits)
 
 template <typename T, int NPER, int ROUTE>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(
@@ -138,14 +139,27 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void topk_kernel(
     const bool live = t < T_;                  // (no early exit: all waves meet the barriers)
     const int lane = threadIdx.x & 63;
     const size_t stride = (size_t)T_ * E;
+    // every split's partial is loaded before any is added (one memory latency instead of
+    // splits x NPER dependent ones), then they are added in split order
     uint64_t key[NPER], orig[NPER];
+    float pv[NPER][kMaxSplits];
+    const float* row = partials + (size_t)t * E;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+        const int e = lane + kWave * i;
+        const bool in = live && e < E;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+            pv[i][sp] = in && sp < splits ? row[sp * stride + e] : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
         const int e = lane + kWave * i;
         if (live && e < E) {
-            const float* row = partials + (size_t)t * E;
-            float l = row[e];
-            for (int sp = 1; sp < splits; ++sp) l += row[sp * stride + e];
+            float l = pv[i][0];
+#pragma unroll
+            for (int sp = 1; sp < kMaxSplits; ++sp)
+                if (sp < splits) l += pv[i][sp];
             if (bias) l += bias[e];
             key[i] = make_key(l, e);
         } else {
