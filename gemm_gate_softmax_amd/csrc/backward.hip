@@ -16,8 +16,9 @@
 // dxd take the weights K-major, and each expert's weight gradient is one GEMM over its own
 // rows with both row-major operands read K-major (the transpose happens in the LDS
 // fragment read; the last k-slice reads zeros past the expert's rows).  Only dWg reads x
-// and the logit gradients transposed into a column block.  All accumulation is fp32; every gradient tensor is rounded once to its storage
-// type (dbias, dw and dl stay fp32).  Deterministic: no atomics.
+// and the logit gradients transposed into a column block.  All accumulation is fp32;
+// every gradient tensor is rounded once to its storage type (dbias, dw and dl stay fp32).
+// Deterministic: no atomics.
 #include "device.h"
 #include "launch.h"
 
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict
     dag[p * 2 * fchunks + fchunks + fc] = pack16(dg, T{});
 }
 
-// ---- segment transposes (64 x 64 tiles through LDS, 16-byte global accesses) ----
+// ---- transposes (64 x 64 tiles through LDS, 16-byte global accesses) ----
 // Every transposed dimension here is a multiple of 64, so tiles are whole.  A thread reads
 // 16-byte chunks of source rows into LDS (one 32-bit word per element, rows padded by one
 // word), then gathers 16 bytes of a destination row from consecutive source rows.
@@ -272,13 +273,10 @@ struct TileIO {
     }
 };
 
-// Segment transpose: out[c][q] = in[src(q)][c] for q < kmax, with src(q) = row pmap[q]
-// (through gather when not NULL) or zero where pmap[q] < 0; pmap NULL: q itself for q < R.
-// C and kmax are multiples of 64.
+// Transpose into a zero-padded column block: out[c][q] = in[q][c] for q < R, 0 for R <= q
+// < kmax.  C and kmax are multiples of 64.
 template <typename T>
 __global__ __launch_bounds__(256) void seg_transpose_kernel(const T* __restrict__ in, int C,
-                                                            const int32_t* __restrict__ gather,
-                                                            const int32_t* __restrict__ pmap,
                                                             int R, int kmax, T* __restrict__ out) {
     using IO = TileIO<T>;
     constexpr int kPer = IO::kPer, kCpr = kTile / kPer;
@@ -287,10 +285,8 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(const T* __restrict_
     for (int i = threadIdx.x; i < IO::kChunks; i += 256) {
         const int r = i / kCpr, cc = i - r * kCpr;
         const int q = q0 + r;
-        int p = pmap ? pmap[q] : (q < R ? q : -1);
-        if (p >= 0 && gather) p = gather[p];
-        const uint4 v = p >= 0 ? *reinterpret_cast<const uint4*>(in + (size_t)p * C + c0 + cc * kPer)
-                               : make_uint4(0, 0, 0, 0);
+        const uint4 v = q < R ? *reinterpret_cast<const uint4*>(in + (size_t)q * C + c0 + cc * kPer)
+                              : make_uint4(0, 0, 0, 0);
         IO::put(tile, r, cc * kPer, v);
     }
     __syncthreads();
@@ -375,11 +371,10 @@ __global__ __launch_bounds__(1024) void split_experts_kernel(const int32_t* __re
 }
 
 template <typename T>
-hipError_t seg_transpose(const void* in, int C, const int32_t* gather, const int32_t* pmap, int R,
-                         int kmax, void* out, hipStream_t s) {
+hipError_t seg_transpose(const void* in, int C, int R, int kmax, void* out, hipStream_t s) {
     const dim3 grid((kmax + kTile - 1) / kTile, (C + kTile - 1) / kTile);
     hipLaunchKernelGGL(seg_transpose_kernel<T>, grid, dim3(256), 0, s, static_cast<const T*>(in),
-                       C, gather, pmap, R, kmax, static_cast<T*>(out));
+                       C, R, kmax, static_cast<T*>(out));
     return hipGetLastError();
 }
 
@@ -483,7 +478,7 @@ hipError_t layer_backward_t(const BwdParams& b, hipStream_t s) {
     hipLaunchKernelGGL(set_gofs_kernel, dim3(1), dim3(64), 0, s, w.gofs, w.tpad, w.zero);
     MOE_CHECK(hipGetLastError());
     // weight gradients: experts with at most kOuterRows rows (or none) as outer products,
-    // the others on the tile GEMM over their column blocks
+    // the others on the tile GEMM over their rows
     hipLaunchKernelGGL(split_experts_kernel, dim3(1), dim3(1024), 0, s, b.counts, E, kOuterRows,
                        w.elist, w.nlist);
     MOE_CHECK(hipGetLastError());
@@ -518,7 +513,7 @@ hipError_t layer_backward_t(const BwdParams& b, hipStream_t s) {
     hipLaunchKernelGGL(gate_dlt_kernel<T>, dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, s, w.dl,
                        b.top_experts, T_, E, k, w.tpad, static_cast<T*>(w.dlt));
     MOE_CHECK(hipGetLastError());
-    MOE_CHECK(seg_transpose<T>(b.x, H, nullptr, nullptr, T_, w.tpad, w.xt, s));
+    MOE_CHECK(seg_transpose<T>(b.x, H, T_, w.tpad, w.xt, s));
     MOE_CHECK(launch_wgrad(dt, 1, E, H, w.tpad, w.dlt, w.xt, w.gofs, nullptr, nullptr, b.dwg, s));
     hipLaunchKernelGGL(gate_dbias_kernel, dim3(E), dim3(256), 0, s, w.dl, b.offsets, b.token_ids,
                        b.dest_pos, k, b.dbias);
