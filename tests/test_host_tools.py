@@ -1,6 +1,6 @@
 """Host-side tools around the benchmark (CPU only): the single-GPU guard of bench.py and the
-counter summaries whose HBM-traffic figure bench.py reports only while the kernel sources
-still hash to what was profiled."""
+counter summaries: the fabric-bytes figure bench.py reports only while the kernel sources
+still hash to what was profiled, the layer-step gaps and the per-dispatch counter means."""
 import argparse
 import csv
 import json
@@ -101,3 +101,19 @@ def test_layer_steps_durations_and_gaps(tmp_path):
     md = ps.steps_markdown(a)
     assert "| 1 | `mid_k(int)` | 5.0 | 2.0 |" in md and "| 2 | `last_k(int)` | 7.0 | 3.0 |" in md
     assert "Step span 27.0 us: kernels 22.0 us, gaps 5.0 us" in md
+
+
+def test_counter_means_sum_instances_and_average_last_dispatches(tmp_path):
+    k = "void expert_gemm_kernel<moe::bf16_t, 2, 1, 128, 128, 3, 128, false>(...)"
+    rows = []
+    for disp, base in ((1, 100.0), (2, 10.0), (3, 20.0)):
+        for inst in range(2):                     # two instances (e.g. XCDs) per dispatch
+            rows.append({"Kernel_Name": k, "Dispatch_Id": disp, "Counter_Name": "TCC_HIT",
+                         "Counter_Value": base + inst})
+        rows.append({"Kernel_Name": "other", "Dispatch_Id": disp + 10, "Counter_Name": "TCC_HIT",
+                     "Counter_Value": 1e9})
+    path = _csv(tmp_path / "c.csv", rows)
+    means, n = ps.counter_means(str(path), "expert_gemm_kernel<moe::bf16_t, 2, 1", 2)
+    assert n == 2
+    # dispatches 2 and 3: (10 + 11) and (20 + 21), mean 31
+    assert means == {"TCC_HIT": 31.0}
