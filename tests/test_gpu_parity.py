@@ -498,6 +498,35 @@ def _weights_host(d, experts, dt):
     return out
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("seed", [1, 2])
+@pytest.mark.parametrize("name", ["xmoe_small", "xmoe_medium", "xmoe_large", "xmoe_super"])
+def test_routing_full_size_more_seeds(orc, name, seed):
+    """Other draws of the full-size layers (near ties fall elsewhere): the fused layer's
+    routing on every token and every buffer array bit-exact against the oracle, routing
+    weights within tolerance."""
+    cfg = W.CONFIGS[name]
+    dt = cfg.dtype
+    _log(f"[routing] {name} seed {seed}: generating inputs")
+    d = W.make_device(cfg, seed=seed, device=DEV)
+    out, bufs, ws = ops.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"],
+                                          cfg.k, fuse_dispatch=True)
+    torch.cuda.synchronize()
+    x_h, wg_h = host(d["x"], dt), host(d["wg"], dt)
+    bias_h = None if d["bias"] is None else host(d["bias"])
+    del d, out
+    te_ref, tw_ref, _, l64 = orc.gate_topk(dt, x_h, wg_h, bias_h, cfg.k, want_logits=True)
+    te, tw = host(bufs["top_experts"]), host(bufs["top_weights"])
+    r = compare_routing(te, te_ref, l64, cfg.k)
+    _log(f"[routing] {name} seed {seed}: {routing_note(r, ws_word(ws, 1))}")
+    assert len(r["mismatch"]) == 0
+    assert float(np.max(np.abs(tw - tw_ref))) <= WEIGHT_ATOL
+    b_ref = orc.pft_build(te_ref, cfg.E)
+    for n in ("counts", "offsets", "token_ids", "expert_ids", "dest_pos"):
+        assert np.array_equal(host(bufs[n]), b_ref[n]), n
+    _log(f"[routing] {name} seed {seed}: {W.routing_summary(b_ref['counts'])}")
+
+
 EVERY_ROW = ["top2_f32", "xmoe_small", "xmoe_medium", "xmoe_large"]
 
 
