@@ -527,19 +527,21 @@ def test_routing_full_size_more_seeds(orc, name, seed):
     _log(f"[routing] {name} seed {seed}: {W.routing_summary(b_ref['counts'])}")
 
 
-EVERY_ROW = ["top2_f32", "xmoe_small", "xmoe_medium", "xmoe_large"]
+EVERY_ROW = [("top2_f32", 0), ("xmoe_small", 0), ("xmoe_medium", 0), ("xmoe_large", 0),
+             ("top2_f32", 1), ("xmoe_small", 1), ("xmoe_medium", 1)]
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", EVERY_ROW)
-def test_layer_full_size_every_row(orc, name):
-    """The layer as the benchmark times it (seed 0, dispatch fused into the up product),
-    compared with the oracle on every token and every buffer row: routing and all buffer
-    arrays bit-exact, routing weights, h and y of all N rows, and out of all T tokens."""
+@pytest.mark.parametrize("name,seed", EVERY_ROW)
+def test_layer_full_size_every_row(orc, name, seed):
+    """The layer as the benchmark times it (seed 0; also a second draw of the smaller
+    configurations; dispatch fused into the up product), compared with the oracle on every
+    token and every buffer row: routing and all buffer arrays bit-exact, routing weights, h
+    and y of all N rows, and out of all T tokens."""
     cfg = W.CONFIGS[name]
     dt = cfg.dtype
-    _log(f"[every row] {name}: generating inputs")
-    d = W.make_device(cfg, seed=0, device=DEV)
+    _log(f"[every row] {name} seed {seed}: generating inputs")
+    d = W.make_device(cfg, seed=seed, device=DEV)
     out, bufs, ws = ops.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"],
                                           cfg.k, fuse_dispatch=True)
     torch.cuda.synchronize()
@@ -550,14 +552,14 @@ def test_layer_full_size_every_row(orc, name):
     te_ref, tw_ref, _, l64 = orc.gate_topk(dt, x_h, wg_h, bias_h, cfg.k, want_logits=True)
     te, tw = host(bufs["top_experts"]), host(bufs["top_weights"])
     r = compare_routing(te, te_ref, l64, cfg.k)
-    _log(f"[every row] {name}: {routing_note(r, ws_word(ws, 1))}")
+    _log(f"[every row] {name} seed {seed}: {routing_note(r, ws_word(ws, 1))}")
     assert len(r["mismatch"]) == 0
     dw = float(np.max(np.abs(tw - tw_ref)))
     assert dw <= WEIGHT_ATOL, dw
     b_ref = orc.pft_build(te_ref, cfg.E)
     for n in ("counts", "offsets", "token_ids", "expert_ids", "dest_pos"):
         assert np.array_equal(host(bufs[n]), b_ref[n]), n
-    _log(f"[every row] {name}: routing {W.routing_summary(b_ref['counts'])}; "
+    _log(f"[every row] {name} seed {seed}: routing {W.routing_summary(b_ref['counts'])}; "
          f"max |dw| {dw:.2e}; oracle experts over all {cfg.N} rows")
     active = np.flatnonzero(b_ref["counts"])
     w = _weights_host(d, active, dt)
@@ -567,7 +569,7 @@ def test_layer_full_size_every_row(orc, name):
     out_ref = orc.combine(dt, y_ref, b_ref["dest_pos"], tw_ref)
     h, y, o = host(bufs["h"], dt), host(bufs["y"], dt), host(out, dt)
     eh, ey, eo = max_abs_rel(h, h_ref, dt), max_abs_rel(y, y_ref, dt), max_abs_rel(o, out_ref, dt)
-    _log(f"[every row] {name}: max-abs-rel err h {eh:.2e} y {ey:.2e} out {eo:.2e} "
+    _log(f"[every row] {name} seed {seed}: max-abs-rel err h {eh:.2e} y {ey:.2e} out {eo:.2e} "
          f"(rms {rms_rel(h, h_ref, dt):.2e} / {rms_rel(y, y_ref, dt):.2e} / "
          f"{rms_rel(o, out_ref, dt):.2e}); tolerance {TOL[dt]:g}")
     assert eh <= TOL[dt] and ey <= TOL[dt] and eo <= TOL[dt]
