@@ -15,6 +15,8 @@ per-stage table goes to stderr first.
   python bench.py --up-kernel-only     # one staged layer, then only the up-product calls
                                        # (the launches the traffic counters are read on)
   python bench.py --dense              # the tile engine vs torch.matmul on dense products
+  python bench.py --memory-ceilings    # how fast one workgroup per CU can read 16 bytes a
+                                       # lane from the L2s, the Infinity Cache and HBM
 
 The roofline object covers the dominant kernel, the expert gate/up product with its
 SwiGLU epilogue (two thirds of the layer's flops), timed on its own through the same
@@ -73,6 +75,10 @@ def parse():
     ap.add_argument("--dense", action="store_true",
                     help="the tile engine on dense single-expert products against torch.matmul "
                          "(hipBLASLt) on the same shapes, as a ceiling reference")
+    ap.add_argument("--memory-ceilings", action="store_true",
+                    help="read rates of the loads the tile engine issues (libmoe_probe.so): "
+                         "direct-to-LDS and plain, 4 and 8 issuing waves per CU, from regions "
+                         "held in the L2s, in the Infinity Cache and in HBM")
     ap.add_argument("--weight-stream", action="store_true",
                     help="the up product on a routing of one row per expert for every expert of "
                          "the workload: a pure stream of the expert weights (for counter runs)")
@@ -307,6 +313,53 @@ def dense(args, dev):
     return 0
 
 
+CEILING_REGIONS = ((1 << 20, "1 MiB (L2)"), (64 << 20, "64 MiB (Infinity Cache)"),
+                   (1 << 30, "1 GiB (HBM)"))
+
+
+def memory_ceilings(args):
+    """moe_probe_stream from libmoe_probe.so (a measurement library, not part of libmoe.so):
+    256 workgroups, one per CU, each reading 1500 slices of 48 KiB round-robin from a region,
+    16 bytes per lane, either as direct-to-LDS transfers into a 3-slot ring (the engine's
+    loaders) or as plain loads into registers.  Median of 5 timed launches after one warm-up."""
+    import ctypes
+
+    import torch
+
+    from gemm_gate_softmax_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        raise RuntimeError(f"{B.PROBE_LIB} is missing: run the build first")
+    probe = ctypes.CDLL(B.PROBE_LIB)
+    probe.moe_probe_stream.restype = ctypes.c_int
+    probe.moe_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    grid, iters, slice_bytes = 256, 1500, 48 * 1024
+    buf = torch.full((1 << 30,), 1, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(grid * 8 * 64, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    rows = []
+    for region, label in CEILING_REGIONS:
+        for kind, kname in ((0, "direct-to-LDS"), (1, "plain loads")):
+            for waves in (4, 8):
+                call = lambda: probe.moe_probe_stream(kind, waves, buf.data_ptr(), region, grid,
+                                                      iters, sink.data_ptr(), stream.cuda_stream)
+                if call() != 0:
+                    raise RuntimeError("moe_probe_stream refused its arguments")
+                torch.cuda.synchronize()
+                ms = time_steps(call, 5, stream)["median"]
+                total = grid * iters * slice_bytes / (ms * 1e-3)
+                rows.append({"region": label, "kind": kname, "waves_per_cu": waves,
+                             "TBs": round(total / 1e12, 2),
+                             "GBs_per_cu": round(total / grid / 1e9, 1),
+                             "GBs_per_wave": round(total / grid / waves / 1e9, 1)})
+                log(f"{label:24s} {kname:14s} {waves} waves/CU: {rows[-1]['TBs']:.2f} TB/s, "
+                    f"{rows[-1]['GBs_per_cu']:.1f} GB/s per CU")
+    print(json.dumps({"memory_ceilings": rows, "grid": grid, "bytes_per_workgroup":
+                      iters * slice_bytes}), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -317,6 +370,8 @@ def main():
 
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.memory_ceilings:
+        return memory_ceilings(args)
 
     import torch
 

@@ -1,8 +1,9 @@
 """Build libmoe.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-``python -m gemm_gate_softmax_amd.build`` compiles every ``csrc/*.hip`` with hipcc and links
-them into ``gemm_gate_softmax_amd/libmoe.so``.  Compilation runs in parallel; objects go to
-``gemm_gate_softmax_amd/_build``.
+``python -m gemm_gate_softmax_amd.build`` compiles the library's ``csrc/*.hip`` with hipcc and
+links them into ``gemm_gate_softmax_amd/libmoe.so``; ``csrc/probe.hip`` (memory-path ceilings
+for ``bench.py --memory-ceilings``, not part of the library) becomes ``libmoe_probe.so``.
+Compilation runs in parallel; objects go to ``gemm_gate_softmax_amd/_build``.
 """
 from __future__ import annotations
 
@@ -17,6 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["api.hip", "gemm.hip", "gate.hip", "pft.hip", "move.hip", "backward.hip"]
+PROBE_SOURCE = "probe.hip"
+PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")
 ARCH = "gfx950"
 
 # Packed fp32 vector ops are switched off for all device code (the compiler otherwise
@@ -41,18 +44,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + [PROBE_SOURCE]
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

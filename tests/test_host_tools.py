@@ -117,3 +117,27 @@ def test_counter_means_sum_instances_and_average_last_dispatches(tmp_path):
     assert n == 2
     # dispatches 2 and 3: (10 + 11) and (20 + 21), mean 31
     assert means == {"TCC_HIT": 31.0}
+
+
+def test_probe_library_exports_its_entry_point_and_rejects_bad_arguments():
+    """libmoe_probe.so (memory-path ceilings for bench.py --memory-ceilings) is built beside
+    libmoe.so; argument checks run before any HIP call, so they can be exercised on the CPU."""
+    import ctypes
+
+    from gemm_gate_softmax_amd import build as B
+    assert os.path.exists(B.PROBE_LIB), "run the build first"
+    probe = ctypes.CDLL(B.PROBE_LIB)
+    f = probe.moe_probe_stream
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    good = dict(kind=0, waves=4, buf=4096, region=1 << 20, grid=256, iters=1, sink=8192)
+    bad = [dict(kind=2), dict(waves=6), dict(buf=0), dict(buf=4100), dict(region=48 * 1024 - 128),
+           dict(region=1 << 40),
+           dict(grid=0), dict(grid=5000), dict(iters=0), dict(sink=0)]
+    for change in bad:
+        a = {**good, **change}
+        assert f(a["kind"], a["waves"], a["buf"], a["region"], a["grid"], a["iters"], a["sink"],
+                 None) == 1, change
+    # the library that the product path loads does not contain the probe
+    assert not hasattr(ctypes.CDLL(B.LIB), "moe_probe_stream")
