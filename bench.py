@@ -14,6 +14,7 @@ per-stage table goes to stderr first.
   python bench.py --calibrate-copy     # plain 1 GiB device copies, for HBM byte counters
   python bench.py --up-kernel-only     # one staged layer, then only the up-product calls
                                        # (the launches the traffic counters are read on)
+  python bench.py --expert-kernels-only  # the same with both products (up, then down)
   python bench.py --dense              # the tile engine vs torch.matmul on dense products
   python bench.py --memory-ceilings    # how fast one workgroup per CU can read 16 bytes a
                                        # lane from the L2s, the Infinity Cache and HBM
@@ -70,6 +71,9 @@ def parse():
                     help="skip timing moe_layer_backward (reported beside the forward)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain device copies of 1 GiB (counter calibration)")
+    ap.add_argument("--expert-kernels-only", action="store_true",
+                    help="like --up-kernel-only with both expert products per call (counter "
+                         "runs of the down product)")
     ap.add_argument("--up-kernel-only", action="store_true",
                     help="one staged layer, then --steps calls of the up product alone")
     ap.add_argument("--dense", action="store_true",
@@ -396,16 +400,20 @@ def main():
     out = torch.empty_like(d["x"])
     stream = torch.cuda.current_stream()
 
-    if args.up_kernel_only:
+    if args.up_kernel_only or args.expert_kernels_only:
         step_staged_once = lambda: ops.moe_layer_forward(
             d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k, out=out, bufs=bufs, ws=ws)
         step_staged_once()
         gws0 = ops.workspace(ops.MOE_WS_GEMM, cfg.N, cfg.H, cfg.E, cfg.F, 1, dtc, dev)
-        for _ in range(args.steps):     # the up product as the layer runs it (dispatch fused)
-            ops.moe_grouped_gemm_swiglu(d["x"], bufs["offsets"], d["w1"], d["w3"], None,
-                                        h=bufs["h"], ws=gws0, token_ids=bufs["token_ids"])
+        both = args.expert_kernels_only
+        for _ in range(args.steps):     # the products as the layer runs them (dispatch fused)
+            ops.moe_grouped_gemm_swiglu(d["x"], bufs["offsets"], d["w1"], d["w3"],
+                                        d["w2"] if both else None, h=bufs["h"],
+                                        y=bufs["y"] if both else None, ws=gws0,
+                                        token_ids=bufs["token_ids"])
         torch.cuda.synchronize()
-        print(json.dumps({"up_kernel_only": args.steps, "workload": cfg.name}), flush=True)
+        print(json.dumps({"expert_kernels_only" if both else "up_kernel_only": args.steps,
+                          "workload": cfg.name}), flush=True)
         return 0
 
     def step():          # the layer with the dispatch fused into the up product
