@@ -148,7 +148,9 @@ def test_combine_parity(orc, dt, T, k, H):
 # ------------------------------------------------------------------------------ gate
 
 GATE_SHAPES = [(1, 64, 8, 1), (200, 256, 8, 2), (333, 512, 64, 6), (256, 1024, 256, 8),
-               (64, 128, 1000, 8), (130, 192, 6, 6), (64, 64, 64, 64)]
+               (64, 128, 1000, 8), (130, 192, 6, 6), (64, 64, 64, 64),
+               # k = 64 < E: the first expert left out is the 65th pick, beyond the wave's lanes
+               (96, 256, 200, 64)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -330,6 +332,10 @@ SMALL_LAYERS = [
     W.LayerConfig("small_f32", T=200, H=128, E=24, F=320, k=6, dtype="f32", bias=("zipf", 1.0)),
     # the most experts the ABI takes: nearly every expert has a handful of rows
     W.LayerConfig("wide_bf16", T=256, H=128, E=1024, F=128, k=8, dtype="bf16", bias=("zipf", 1.2)),
+    # the most picks per token the ABI takes, with experts left out
+    W.LayerConfig("max_k_bf16", T=96, H=128, E=128, F=64, k=64, dtype="bf16", bias=("zipf", 1.0)),
+    # the smallest H and F: every product is a single k-slice
+    W.LayerConfig("min_dims_bf16", T=500, H=64, E=16, F=64, k=4, dtype="bf16", bias=("zipf", 1.2)),
 ]
 
 
