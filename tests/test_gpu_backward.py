@@ -44,6 +44,13 @@ CASES = [
     # operands, expert offsets not multiples of 64, ragged last k-slices
     (W.LayerConfig("rows_f32", T=333, H=192, E=5, F=128, k=2, dtype="f32"), "softmax"),
     (W.LayerConfig("rows_bf16", T=333, H=192, E=5, F=128, k=2, dtype="bf16"), "softmax"),
+    # the smallest H and F: every K-major product is one k-slice (dxd reads W1 for its first
+    # slice and W3 for its second)
+    (W.LayerConfig("min_dims_bf16", T=500, H=64, E=16, F=64, k=4, dtype="bf16",
+                   bias=("zipf", 1.2)), "softmax"),
+    # the most picks per token, with experts left out
+    (W.LayerConfig("max_k_bf16", T=96, H=128, E=128, F=64, k=64, dtype="bf16",
+                   bias=("zipf", 1.0)), "softmax"),
 ]
 
 
