@@ -325,7 +325,8 @@ def memory_ceilings(args):
     """moe_probe_stream from libmoe_probe.so (a measurement library, not part of libmoe.so):
     256 workgroups, one per CU, each reading 1500 slices of 48 KiB round-robin from a region,
     16 bytes per lane, either as direct-to-LDS transfers into a 3-slot ring (the engine's
-    loaders) or as plain loads into registers.  Median of 5 timed launches after one warm-up."""
+    loaders) or as plain loads into registers, or writing them with plain stores.  Median of
+    5 timed launches after one warm-up."""
     import ctypes
 
     import torch
@@ -344,7 +345,7 @@ def memory_ceilings(args):
     stream = torch.cuda.current_stream()
     rows = []
     for region, label in CEILING_REGIONS:
-        for kind, kname in ((0, "direct-to-LDS"), (1, "plain loads")):
+        for kind, kname in ((0, "direct-to-LDS"), (1, "plain loads"), (2, "plain stores")):
             for waves in (4, 8):
                 call = lambda: probe.moe_probe_stream(kind, waves, buf.data_ptr(), region, grid,
                                                       iters, sink.data_ptr(), stream.cuda_stream)

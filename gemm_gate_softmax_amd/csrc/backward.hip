@@ -303,10 +303,13 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(const T* __restrict_
 // b[src(p_i)][f], p_i = offsets[e] + i, src = gather[p] or p, fp32 FMAs in ascending i, one
 // rounding.  One workgroup per (expert, kOuterM output rows); each thread takes 16-byte
 // chunks of f, so every store instruction writes whole row segments; the rows it reads are
-// the untransposed ones.  Experts without rows get zeros; larger experts are left to the
-// tile GEMM.
+// the untransposed ones.  The expert's source rows and its a values (the same for every
+// thread) are staged in LDS once, and the b chunks of kOuterBatch rows are loaded before
+// any of their FMAs, so a pass over f waits for about r / kOuterBatch memory latencies
+// rather than r.  Experts without rows get zeros; larger experts are left to the tile GEMM.
 constexpr int kOuterRows = 64;
 constexpr int kOuterM = 16;
+constexpr int kOuterBatch = 4;
 
 template <typename T>
 __global__ __launch_bounds__(256) void wgrad_outer_kernel(const T* __restrict__ a, int lda, int aoff,
@@ -315,9 +318,16 @@ __global__ __launch_bounds__(256) void wgrad_outer_kernel(const T* __restrict__ 
                                                           const int32_t* __restrict__ offsets,
                                                           int M, int Nf, T* __restrict__ out) {
     constexpr int P = 16 / (int)sizeof(T);
+    constexpr int Q = kOuterM / P;                  // 16-byte chunks of a per row
+    __shared__ int src_s[kOuterRows];
+    __shared__ uint4 a_s[kOuterRows][Q];
     const int e = blockIdx.y, m0 = blockIdx.x * kOuterM;
     const int p0 = offsets[e], r = offsets[e + 1] - p0;
     if (r > kOuterRows) return;                     // whole workgroup
+    for (int i = threadIdx.x; i < r; i += 256) src_s[i] = gather ? gather[p0 + i] : p0 + i;
+    for (int j = threadIdx.x; j < r * Q; j += 256)
+        a_s[j / Q][j % Q] = reinterpret_cast<const uint4*>(a + (size_t)(p0 + j / Q) * lda + aoff + m0)[j % Q];
+    __syncthreads();
     T* o = out + ((size_t)e * M + m0) * Nf;
     const int nfc = Nf / P;
     for (int fc = threadIdx.x; fc < nfc; fc += 256) {
@@ -326,20 +336,26 @@ __global__ __launch_bounds__(256) void wgrad_outer_kernel(const T* __restrict__ 
         for (int mm = 0; mm < kOuterM; ++mm)
 #pragma unroll
             for (int v = 0; v < P; ++v) acc[mm][v] = 0.0f;
-        for (int i = 0; i < r; ++i) {
-            const int p = p0 + i;
-            const int src = gather ? gather[p] : p;
-            float bv[P];
-            unpack16(*reinterpret_cast<const uint4*>(b + (size_t)src * ldb + (size_t)fc * P), bv, T{});
-            const uint4* arow = reinterpret_cast<const uint4*>(a + (size_t)p * lda + aoff + m0);
+        for (int i0 = 0; i0 < r; i0 += kOuterBatch) {
+            uint4 bq[kOuterBatch];
 #pragma unroll
-            for (int q = 0; q < kOuterM / P; ++q) {
-                float av[P];
-                unpack16(arow[q], av, T{});
+            for (int u = 0; u < kOuterBatch; ++u)
+                if (i0 + u < r)
+                    bq[u] = *reinterpret_cast<const uint4*>(b + (size_t)src_s[i0 + u] * ldb + (size_t)fc * P);
 #pragma unroll
-                for (int u = 0; u < P; ++u)
+            for (int u = 0; u < kOuterBatch; ++u) {
+                if (i0 + u >= r) break;
+                float bv[P];
+                unpack16(bq[u], bv, T{});
 #pragma unroll
-                    for (int v = 0; v < P; ++v) acc[q * P + u][v] = fmaf(av[u], bv[v], acc[q * P + u][v]);
+                for (int q = 0; q < Q; ++q) {
+                    float av[P];
+                    unpack16(a_s[i0 + u][q], av, T{});
+#pragma unroll
+                    for (int w = 0; w < P; ++w)
+#pragma unroll
+                        for (int v = 0; v < P; ++v) acc[q * P + w][v] = fmaf(av[w], bv[v], acc[q * P + w][v]);
+                }
             }
         }
 #pragma unroll

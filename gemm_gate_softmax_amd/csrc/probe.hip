@@ -3,7 +3,7 @@
 // One workgroup per CU (grid 256) reads a region of R bytes round-robin with 16 bytes per
 // lane, either the way the engine's loader waves do (direct-to-LDS transfers into a
 // 3-slot ring of 48 KiB k-slices, at most two slices outstanding per wave) or as plain
-// vector loads into registers.  A region of 1 MiB stays in every XCD's L2, 64 MiB fits the
+// vector loads into registers; or writes it the same way with plain 16-byte stores.  A region of 1 MiB stays in every XCD's L2, 64 MiB fits the
 // Infinity Cache, 1 GiB streams from HBM.  The rate per CU for 4 and 8 issuing waves and
 // the chip's total show what bounds a kernel that moves its operands this way.
 //
@@ -11,7 +11,8 @@
 // loads.  C ABI:
 //   int moe_probe_stream(int kind, int waves, const void* buf, long long region_bytes,
 //                        int grid, int iters, int* sink, void* stream)
-//   kind 0: direct-to-LDS, 1: plain loads; waves 4 or 8; buf: device, 16-byte aligned,
+//   kind 0: direct-to-LDS, 1: plain loads, 2: plain stores (buf is overwritten); waves 4 or
+//   8; buf: device, 16-byte aligned,
 //   region_bytes readable bytes, 48 KiB to 256 GiB; sink: device, grid * waves * 64 ints;
 //   each workgroup reads iters x 48 KiB.  Returns 0, 1 for a bad argument, 2 when the
 //   launch fails.  The launch goes to `stream` and is not waited for.
@@ -108,12 +109,37 @@ __global__ __launch_bounds__(NW * 64, 1) void reg_stream_kernel(const uint4* buf
     sink[blockIdx.x * NW * 64 + threadIdx.x] = (int)(acc.x ^ acc.y ^ acc.z ^ acc.w);
 }
 
+// The same blocks written: every lane stores 16 bytes per block, kPer stores per slice.
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void reg_store_kernel(uint4* buf, int rows, int iters,
+                                                               int* sink) {
+    constexpr int kPer = kSliceRows / 8 / NW;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long long start = (long long)blockIdx.x * kSliceRows * 7;
+    int row[kPer], chunk[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int r = (w * kPer + i) * 8 + lane / 8;
+        row[i] = (int)((start + r) % rows);
+        chunk[i] = (lane & 7) ^ ((r >> 1) & 7);
+    }
+    const uint4 v = make_uint4(blockIdx.x, threadIdx.x, 0, 1);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            buf[(size_t)row[i] * 8 + chunk[i]] = v;
+            row[i] = next_row(row[i], rows);
+        }
+    }
+    sink[blockIdx.x * NW * 64 + threadIdx.x] = row[0];
+}
+
 }  // namespace
 
 extern "C" __attribute__((visibility("default"))) int moe_probe_stream(
     int kind, int waves, const void* buf, long long region_bytes, int grid, int iters, int* sink,
     void* stream) {
-    if ((kind != 0 && kind != 1) || (waves != 4 && waves != 8) || !buf || !sink ||
+    if ((kind < 0 || kind > 2) || (waves != 4 && waves != 8) || !buf || !sink ||
         (reinterpret_cast<uintptr_t>(buf) & 15u) != 0 || region_bytes < kSlice ||
         region_bytes / 128 > 0x7fffffffll || grid < 1 || grid > 4096 || iters < 1)
         return 1;
@@ -125,12 +151,18 @@ extern "C" __attribute__((visibility("default"))) int moe_probe_stream(
             hipLaunchKernelGGL(lds_stream_kernel<4>, dim3(grid), dim3(256), 0, s, b, rows, iters, sink);
         else
             hipLaunchKernelGGL(lds_stream_kernel<8>, dim3(grid), dim3(512), 0, s, b, rows, iters, sink);
-    } else {
+    } else if (kind == 1) {
         const uint4* u = static_cast<const uint4*>(buf);
         if (waves == 4)
             hipLaunchKernelGGL(reg_stream_kernel<4>, dim3(grid), dim3(256), 0, s, u, rows, iters, sink);
         else
             hipLaunchKernelGGL(reg_stream_kernel<8>, dim3(grid), dim3(512), 0, s, u, rows, iters, sink);
+    } else {
+        uint4* u = static_cast<uint4*>(const_cast<void*>(buf));
+        if (waves == 4)
+            hipLaunchKernelGGL(reg_store_kernel<4>, dim3(grid), dim3(256), 0, s, u, rows, iters, sink);
+        else
+            hipLaunchKernelGGL(reg_store_kernel<8>, dim3(grid), dim3(512), 0, s, u, rows, iters, sink);
     }
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }

@@ -132,7 +132,7 @@ def test_probe_library_exports_its_entry_point_and_rejects_bad_arguments():
     f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     good = dict(kind=0, waves=4, buf=4096, region=1 << 20, grid=256, iters=1, sink=8192)
-    bad = [dict(kind=2), dict(waves=6), dict(buf=0), dict(buf=4100), dict(region=48 * 1024 - 128),
+    bad = [dict(kind=3), dict(kind=-1), dict(waves=6), dict(buf=0), dict(buf=4100), dict(region=48 * 1024 - 128),
            dict(region=1 << 40),
            dict(grid=0), dict(grid=5000), dict(iters=0), dict(sink=0)]
     for change in bad:
