@@ -18,6 +18,8 @@ per-stage table goes to stderr first.
   python bench.py --dense              # the tile engine vs torch.matmul on dense products
   python bench.py --memory-ceilings    # how fast one workgroup per CU can read 16 bytes a
                                        # lane from the L2s, the Infinity Cache and HBM
+  python bench.py --ab LIB,LIB,...     # the layer with each library (variants built by
+                                       # gemm_gate_softmax_amd.build --variant), alternating
 
 The roofline object covers the dominant kernel, the expert gate/up product with its
 SwiGLU epilogue (two thirds of the layer's flops), timed on its own through the same
@@ -79,6 +81,11 @@ def parse():
     ap.add_argument("--dense", action="store_true",
                     help="the tile engine on dense single-expert products against torch.matmul "
                          "(hipBLASLt) on the same shapes, as a ceiling reference")
+    ap.add_argument("--ab", default=None,
+                    help="comma-separated libmoe builds (variants from gemm_gate_softmax_amd.build "
+                         "--variant): the fused layer, its up product and both expert products "
+                         "timed with each, alternating, outputs compared with the first's")
+    ap.add_argument("--ab-reps", type=int, default=3)
     ap.add_argument("--memory-ceilings", action="store_true",
                     help="read rates of the loads the tile engine issues (libmoe_probe.so): "
                          "direct-to-LDS and plain, 4 and 8 issuing waves per CU, from regions "
@@ -365,6 +372,72 @@ def memory_ceilings(args):
     return 0
 
 
+def ab_compare(cfg, args, dev):
+    """The fused layer, the up product as the layer runs it, and both expert products, with
+    each library in turn (rounds alternate between them); each library's h, y and out are
+    compared with the first library's: bit-identical, or the max-abs-rel error."""
+    import torch
+
+    from gemm_gate_softmax_amd import ops
+    from gemm_gate_softmax_amd import workloads as W
+    libs = [os.path.abspath(p) for p in args.ab.split(",") if p]
+    for p in libs:
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing")
+
+    def use(path):
+        ops._lib = None
+        ops.LIB_PATH = path
+        ops.lib()
+
+    d = W.make_device(cfg, seed=args.seed, device=dev)
+    use(libs[0])
+    bufs = ops.alloc_layer_bufs(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, d["x"].dtype, dev,
+                                fuse_dispatch=True)
+    dtc = ops.dtype_code(d["x"].dtype)
+    ws = gws = None
+    for p in libs:                   # workspaces large enough for every variant
+        use(p)
+        w = ops.workspace(ops.MOE_WS_LAYER, cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, dtc, dev)
+        g = ops.workspace(ops.MOE_WS_GEMM, cfg.N, cfg.H, cfg.E, cfg.F, 1, dtc, dev)
+        ws = w if ws is None or w.numel() > ws.numel() else ws
+        gws = g if gws is None or g.numel() > gws.numel() else gws
+    out = torch.empty_like(d["x"])
+    stream = torch.cuda.current_stream()
+    layer = lambda: ops.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"],
+                                          cfg.k, out=out, bufs=bufs, ws=ws)
+    up = lambda: ops.moe_grouped_gemm_swiglu(d["x"], bufs["offsets"], d["w1"], d["w3"], None,
+                                             h=bufs["h"], ws=gws, token_ids=bufs["token_ids"])
+    both = lambda: ops.moe_grouped_gemm_swiglu(d["x"], bufs["offsets"], d["w1"], d["w3"], d["w2"],
+                                               h=bufs["h"], y=bufs["y"], ws=gws,
+                                               token_ids=bufs["token_ids"])
+    ref, res = None, {p: {"layer": [], "up": [], "experts": []} for p in libs}
+    agree = {}
+    for _ in range(max(1, args.ab_reps)):
+        for p in libs:
+            use(p)
+            layer()
+            torch.cuda.synchronize()
+            got = {n: t.float().clone() for n, t in (("h", bufs["h"]), ("y", bufs["y"]), ("out", out))}
+            if ref is None:
+                ref = got
+            if p not in agree:
+                same = all(torch.equal(got[n], ref[n]) for n in got)
+                err = max(float((got[n] - ref[n]).abs().max() / ref[n].abs().max()) for n in got)
+                agree[p] = "bit-identical" if same else f"max-abs-rel {err:.2e}"
+            for name, fn in (("layer", layer), ("up", up), ("experts", both)):
+                fn()
+                torch.cuda.synchronize()
+                res[p][name].append(time_steps(fn, 10, stream)["median"])
+            log(f"ab {cfg.name} {os.path.basename(p)}: layer {res[p]['layer'][-1]:.3f} ms, up "
+                f"{res[p]['up'][-1]:.3f} ms, both products {res[p]['experts'][-1]:.3f} ms")
+    print(json.dumps({"ab": cfg.name, "libs": [
+        {"lib": os.path.relpath(p, ROOT), "outputs_vs_first": agree[p],
+         **{f"{n}_ms_min": round(min(v), 4) for n, v in res[p].items()}} for p in libs]}),
+        flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -388,6 +461,8 @@ def main():
     ops.lib()                                   # the HIP library or nothing
     if args.weight_stream:
         return weight_stream(cfg, args, dev)
+    if args.ab:
+        return ab_compare(cfg, args, dev)
     if args.dense:
         return dense(args, dev)
     log(f"bench: {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} F={cfg.F} k={cfg.k} {cfg.dtype}: "

@@ -4,6 +4,10 @@
 links them into ``gemm_gate_softmax_amd/libmoe.so``; ``csrc/probe.hip`` (memory-path ceilings
 for ``bench.py --memory-ceilings``, not part of the library) becomes ``libmoe_probe.so``.
 Compilation runs in parallel; objects go to ``gemm_gate_softmax_amd/_build``.
+
+``python -m gemm_gate_softmax_amd.build --variant NAME -DMOE_...=V ...`` builds the library
+with the given compile-time switches into ``gemm_gate_softmax_amd/_variants/libmoe_NAME.so``,
+for ``bench.py --ab`` comparisons of the alternatives the sources keep behind switches.
 """
 from __future__ import annotations
 
@@ -20,6 +24,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["api.hip", "gemm.hip", "gate.hip", "pft.hip", "move.hip", "backward.hip"]
 PROBE_SOURCE = "probe.hip"
 PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")
+VARIANTS = os.path.join(HERE, "_variants")
 ARCH = "gfx950"
 
 # Packed fp32 vector ops are switched off for all device code (the compiler otherwise
@@ -35,9 +40,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmoe.so)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, out_dir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *FLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -65,6 +70,23 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_variant(name: str, defines) -> str:
+    """libmoe.so built with extra -D switches into _variants/libmoe_NAME.so."""
+    defines = list(defines)
+    if not name.isidentifier() or any(not d.startswith("-DMOE_") for d in defines):
+        raise ValueError("variant: a plain name and -DMOE_... switches only")
+    out_dir = os.path.join(VARIANTS, name + ".objs")
+    os.makedirs(out_dir, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda src: _compile(src, out_dir, defines), SOURCES))
+    lib = os.path.join(VARIANTS, f"libmoe_{name}.so")
+    _link(objs, lib)
+    return lib
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) > 2 and sys.argv[1] == "--variant":
+        print(f"built {build_variant(sys.argv[2], sys.argv[3:])}")
+    else:
+        build(verbose=True)
     sys.exit(0)

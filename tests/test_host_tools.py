@@ -141,3 +141,15 @@ def test_probe_library_exports_its_entry_point_and_rejects_bad_arguments():
                  None) == 1, change
     # the library that the product path loads does not contain the probe
     assert not hasattr(ctypes.CDLL(B.LIB), "moe_probe_stream")
+
+
+def test_variant_builds_take_library_switches_only():
+    """build_variant compiles only with -DMOE_... switches and a plain name (it writes into the
+    package's _variants folder); anything else is refused before hipcc runs."""
+    import pytest
+
+    from gemm_gate_softmax_amd import build as B
+    for name, defines in (("ok", ["-O0"]), ("ok", ["-DOTHER=1"]), ("../x", ["-DMOE_K_ROTATE=0"]),
+                          ("a b", [])):
+        with pytest.raises(ValueError):
+            B.build_variant(name, defines)
