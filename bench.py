@@ -395,13 +395,15 @@ def ab_compare(cfg, args, dev):
     bufs = ops.alloc_layer_bufs(cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, d["x"].dtype, dev,
                                 fuse_dispatch=True)
     dtc = ops.dtype_code(d["x"].dtype)
-    ws = gws = None
+    ws = gws = gate_ws = None
     for p in libs:                   # workspaces large enough for every variant
         use(p)
         w = ops.workspace(ops.MOE_WS_LAYER, cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, dtc, dev)
         g = ops.workspace(ops.MOE_WS_GEMM, cfg.N, cfg.H, cfg.E, cfg.F, 1, dtc, dev)
+        a = ops.workspace(ops.MOE_WS_GATE, cfg.T, cfg.H, cfg.E, cfg.F, cfg.k, dtc, dev)
         ws = w if ws is None or w.numel() > ws.numel() else ws
         gws = g if gws is None or g.numel() > gws.numel() else gws
+        gate_ws = a if gate_ws is None or a.numel() > gate_ws.numel() else gate_ws
     out = torch.empty_like(d["x"])
     stream = torch.cuda.current_stream()
     layer = lambda: ops.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"],
@@ -411,7 +413,11 @@ def ab_compare(cfg, args, dev):
     both = lambda: ops.moe_grouped_gemm_swiglu(d["x"], bufs["offsets"], d["w1"], d["w3"], d["w2"],
                                                h=bufs["h"], y=bufs["y"], ws=gws,
                                                token_ids=bufs["token_ids"])
-    ref, res = None, {p: {"layer": [], "up": [], "experts": []} for p in libs}
+    te = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    gate = lambda: ops.moe_gate_topk(d["x"], d["wg"], d["bias"], cfg.k, top_experts=te,
+                                     top_weights=tw, ws=gate_ws)
+    ref, res = None, {p: {"layer": [], "up": [], "experts": [], "gate": []} for p in libs}
     agree = {}
     for _ in range(max(1, args.ab_reps)):
         for p in libs:
@@ -425,12 +431,13 @@ def ab_compare(cfg, args, dev):
                 same = all(torch.equal(got[n], ref[n]) for n in got)
                 err = max(float((got[n] - ref[n]).abs().max() / ref[n].abs().max()) for n in got)
                 agree[p] = "bit-identical" if same else f"max-abs-rel {err:.2e}"
-            for name, fn in (("layer", layer), ("up", up), ("experts", both)):
+            for name, fn in (("layer", layer), ("up", up), ("experts", both), ("gate", gate)):
                 fn()
                 torch.cuda.synchronize()
                 res[p][name].append(time_steps(fn, 10, stream)["median"])
             log(f"ab {cfg.name} {os.path.basename(p)}: layer {res[p]['layer'][-1]:.3f} ms, up "
-                f"{res[p]['up'][-1]:.3f} ms, both products {res[p]['experts'][-1]:.3f} ms")
+                f"{res[p]['up'][-1]:.3f} ms, both products {res[p]['experts'][-1]:.3f} ms, gate "
+                f"{res[p]['gate'][-1] * 1e3:.1f} us")
     print(json.dumps({"ab": cfg.name, "libs": [
         {"lib": os.path.relpath(p, ROOT), "outputs_vs_first": agree[p],
          **{f"{n}_ms_min": round(min(v), 4) for n, v in res[p].items()}} for p in libs]}),

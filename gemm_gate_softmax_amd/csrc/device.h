@@ -76,19 +76,39 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, kWave);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, kWave);
+// One DPP lane move of a 64-bit value within each row of 16 lanes (CTRL: a dpp_ctrl code).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, 0xf, 0xf, false));
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, 0xf, 0xf, false));
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// Maximum over the wave's 64 lanes, on every lane.  Within each row of 16 lanes the values
+// meet through DPP lane moves (the lane 1 apart, 2 apart, then the mirrored lane in the half
+// row and in the row), so every lane of a row holds the row's maximum; the four row maxima
+// are read into scalar registers and combined.  No LDS round trip, unlike a shuffle.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    uint64_t o;
+    o = dpp_u64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v = o > v ? o : v;
+    o = dpp_u64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v = o > v ? o : v;
+    o = dpp_u64<0x141>(v);  // row_half_mirror
+    v = o > v ? o : v;
+    o = dpp_u64<0x140>(v);  // row_mirror
+    v = o > v ? o : v;
+    const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+    uint64_t m = 0;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const uint64_t o = shfl_xor_u64(v, m);
-        v = o > v ? o : v;
+    for (int r = 0; r < kWave; r += 16) {
+        const uint64_t x = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), r))) << 32) |
+                           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), r));
+        m = x > m ? x : m;
     }
-    return v;
+    return m;
 }
 
 __device__ __forceinline__ int wave_sum_i32(int v) {
