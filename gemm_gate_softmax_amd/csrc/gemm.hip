@@ -105,6 +105,19 @@ constexpr int kRotPeriod = MOE_K_ROTATE > 0 ? MOE_K_ROTATE : 1;
 // nothing.
 constexpr int kSmallBTok = MOE_SMALL_BTOK;
 constexpr int kSmallStages = MOE_SMALL_STAGES;
+// bf16 expert products (the forward's and the backward's recompute of a and g) run as a
+// persistent tile loop, one workgroup per CU claiming tiles from per-XCD counters, so a
+// tile's start-up (table lookups, the first slices' latency) overlaps the previous tile's
+// epilogue (expert_gemm_kernel, PST).  Measured, fused layer, one-tile-per-workgroup grid
+// against the loop (same box, alternating): X-MoE Small 0.997 / 0.965 ms, Medium 1.743 /
+// 1.714, Large 4.117 / 4.048; the top-2 fp32 layer, whose tiles are four times longer per
+// k-slice, ran 2.243 / 2.282 ms with it, so fp32 keeps one tile per workgroup.  A static
+// schedule (tile i, i + W, ... per workgroup) instead of the counters: X-MoE Large 4.180 ms.
+// 0 switches the loop off.
+#ifndef MOE_PERSIST
+#define MOE_PERSIST 1
+#endif
+constexpr bool kPersist = MOE_PERSIST != 0;
 
 template <typename T, int NB>
 struct GemmParams {
@@ -136,6 +149,7 @@ struct GemmParams {
     int* zero_word;         // dense product: set to 0 by workgroup 0 (nullable)
     int* zero_buf;          // dense product: zero_buf[0, zero_n) set to 0 (nullable)
     int zero_n;
+    int* claim;             // persistent expert grid: 8 per-XCD tile counters, 0 at launch
 };
 
 // Writes 4 consecutive fp32 partial logits of one token (per-element bounds: E need not be
@@ -241,6 +255,7 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
 __device__ __forceinline__ int kmajor_swizzle(int k) { return ((k >> 1) & 1) << 2; }
 
 typedef short moe_v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) int lds_int;
 
 // This lane's weight fragment of a K-major region for features [mrow, mrow + 32) (mrow a
 // multiple of 32) and k-step KSTEP: what the K-contiguous layout's 16-byte read gives, i.e.
@@ -293,11 +308,20 @@ __device__ __forceinline__ uint4 kmajor_frag(const char* region, int mrow, int k
 // the weights are stored K-major (w[b][k][n], rows w_ld apart), see kmajor_frag; AKM: the
 // activations too (act[k][m], rows a_ld apart; the tile's "rows" are then m).  K-major
 // rows at or past k_rows read zeros.
+//
+// LDS_BYTES > 0: one of a run of tiles on the same workgroup (a persistent tile loop over
+// an LDS array of LDS_BYTES).  The epilogue then stages its outputs in the last STG bytes
+// of the array instead of the first, so the loaders can run ahead into the next tile's
+// first stages while the compute waves still store this one: the stages whose slots lie
+// below LDS_BYTES - STG are issued before barrier 0, the rest after it.  A loader lane with
+// a non-null `note` claims the workgroup's next tile once its own transfers are done:
+// it writes next_base + (*claim, incremented) to `note` (LDS) before the tile's last barrier.
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool FULL, bool WNT = false,
-          bool WKM = false, bool AKM = false>
+          bool WKM = false, bool AKM = false, int LDS_BYTES = 0, int STG = 0>
 __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* lds, int expert,
                                              int row0, int row_end, int f0, int s0, int nk,
-                                             int rot = 0) {
+                                             int rot = 0, volatile lds_int* note = nullptr,
+                                             int* claim = nullptr, int next_base = 0) {
     using Tile = CompTile<BT, BF, NB, S, RB>;
     constexpr int kRowBytes = Tile::kRowBytes;
     constexpr int kRowsPerDma = 1024 / kRowBytes;    // rows per 1 KiB DMA instruction
@@ -311,6 +335,12 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
     static_assert(BT % (4 * kRowsPerDma) == 0 && BF % (4 * kRowsPerDma) == 0, "operand blocks");
     static_assert(S >= 2 && (S - 2) * kDma < 64 && S * kStageBytes <= 160 * 1024, "ring");
     static_assert(KS % 2 == 0, "k-steps alternate between the two fragment buffers");
+    constexpr bool kRun = LDS_BYTES > 0;
+    // stages issued before barrier 0 (slots clear of the staging region when kRun)
+    constexpr int kFree = kRun ? (LDS_BYTES - STG) / kStageBytes : S - 1;
+    constexpr int PRE = kFree < S - 1 ? kFree : S - 1;
+    static_assert(PRE >= 1 && (!kRun || (STG > 0 && STG <= LDS_BYTES && S * kStageBytes <= LDS_BYTES)),
+                  "persistent layout");
 
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -400,10 +430,12 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
             MOE_ISSUE(0, 0);
             wait_vm_and_barrier<0, false>();
         } else {
-            for (int s = 0; s < S - 1; ++s) MOE_ISSUE(min(s, nk - 1), s);
+            for (int s = 0; s < PRE; ++s) MOE_ISSUE(min(s, nk - 1), s);
             // barrier 0: stage 0 landed
-            if constexpr (FULL) wait_vm_and_barrier<(S - 2) * kDma, false>();
-            else wait_vm_and_barrier_rt<(S - 2) * (kDma - kActDma), (S - 2) * kDma>((S - 2) * keff);
+            if constexpr (FULL) wait_vm_and_barrier<(PRE - 1) * kDma, false>();
+            else wait_vm_and_barrier_rt<(PRE - 1) * (kDma - kActDma), (PRE - 1) * kDma>((PRE - 1) * keff);
+            // the previous tile's staging is read by now: its slots can be filled
+            for (int s = PRE; s < S - 1; ++s) MOE_ISSUE(min(s, nk - 1), s);
         }
         int refill = S - 1;
         for (int kt = 0; kt < nk - 1; ++kt) {
@@ -422,7 +454,16 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
         }
 #undef MOE_ISSUE
         // (every transfer has landed: the last wait above was for none outstanding)
-        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));           // vmcnt(0)
+        if constexpr (kRun) {
+            // the compute waves are still on the last stage: the claim's latency hides there
+            if (note)
+                *note = next_base + __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("" ::: "memory");                          // the write stays above
+            __builtin_amdgcn_s_waitcnt(7 << 4);                      // vmcnt(0) lgkmcnt(0)
+        } else {
+            __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));       // vmcnt(0)
+        }
         __builtin_amdgcn_s_barrier();                               // ring free: staging
         return;
     }
@@ -549,7 +590,8 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
     constexpr int kPitch = kRowOut + 16;                   // +16: rows 16 apart share banks
     constexpr int kCpr = kRowOut / 16;                     // 16-byte chunks per row
     constexpr int kOutChunks = (BT / 2) * kCpr;
-    static_assert(4 * (BT / 2) * kPitch <= S * kStageBytes && kOutChunks % 64 == 0, "staging");
+    static_assert(4 * (BT / 2) * kPitch <= (kRun ? STG : S * kStageBytes) && kOutChunks % 64 == 0,
+                  "staging");
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (3 << 14));   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     if (EPI == kEpiLogits && (p.n_feat & 3) != 0) {
@@ -571,7 +613,7 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
         }
         return;
     }
-    char* stg = lds + wave * (BT / 2) * kPitch;
+    char* stg = lds + (kRun ? LDS_BYTES - STG : 0) + wave * (BT / 2) * kPitch;
     const int tok0 = row0 + wt * (BT / 2), feat0 = f0 + wf * (BF / 2);
     constexpr int kOuts = EPI == kEpiPair ? 2 : (EPI == kEpiSwiGLUPair ? 3 : 1);
 #pragma unroll
@@ -616,6 +658,9 @@ __device__ __forceinline__ void compute_tile(const GemmParams<T, NB>& p, char* l
                 *reinterpret_cast<uint4*>(out + (size_t)tok * p.n_feat + feat) = v;
         }
     }
+    // (a run of tiles: this wave's staging reads have returned before the next tile's
+    // barrier 0, after which the loaders may refill that region)
+    if constexpr (kRun) __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (3 << 14));   // lgkmcnt(0)
 }
 
 // Dense product (the gate logits): one expert, rows [0, dense_rows), XCD-contiguous tiles.
@@ -666,53 +711,106 @@ constexpr int expert_lds_bytes() {
     return a > b ? a : b;
 }
 
-template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool WKM = false>
+// Bytes of LDS a tile's epilogue stages through (4 compute waves x BT/2 token rows of BF/2
+// outputs, padded), for the persistent tile loop, which keeps them clear of the next tile's
+// first ring slots.
+template <typename T, int BT, int BF>
+constexpr int expert_stg_bytes() {
+    return 4 * (BT / 2) * ((BF / 2) * (int)sizeof(T) + 16);
+}
+
+// Whether a tile run fits: the first ring slot of either tile size lies below the staging
+// region, so a tile can start its transfers while the previous one stages its outputs
+// (bf16 128 x (2 x 128) tiles stage 36 KiB and fill two slots ahead, 128 x 256 tiles stage
+// 68 KiB and fill one; fp32 128 x 256 tiles stage 132 KiB and do not fit).
+template <typename T, int NB, int BT, int BF, int S, int RB>
+constexpr bool expert_run_fits() {
+    constexpr int free_bytes = expert_lds_bytes<BT, BF, NB, S, RB>() - expert_stg_bytes<T, BT, BF>();
+    constexpr int large = CompTile<BT, BF, NB, S, RB>::kStageBytes;
+    constexpr int small = kSmallBTok > 0 ? CompTile<(kSmallBTok > 0 ? kSmallBTok : 64), BF, NB,
+                                                    kSmallStages, RB>::kStageBytes : 0;
+    return free_bytes >= large && free_bytes >= small;
+}
+
+// PST: a persistent grid of one workgroup per CU (8 x W workgroups, W per XCD) walking the
+// same per-XCD tile order as the one-tile-per-workgroup grid.  Workgroup i of XCD x starts
+// with the XCD's tile i; near the end of each tile one loader lane claims the workgroup's
+// next tile, W + (the XCD's counter, incremented), and leaves it in LDS before the tile's
+// last barrier, so tiles go to workgroups as they free up, as the hardware dispatcher would
+// hand them out.  The loader waves start the next tile's transfers while the compute waves
+// store the current one.  Both roles walk the same tile sequence and meet at the same
+// barriers; no workgroup waits on another.
+template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool WKM = false,
+          bool PST = false>
 __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, NB> p) {
-    __shared__ __attribute__((aligned(1024))) char lds[expert_lds_bytes<BT, BF, NB, S, RB>()];
+    constexpr int kLds = expert_lds_bytes<BT, BF, NB, S, RB>();
+    __shared__ __attribute__((aligned(1024))) char lds[kLds];
+    constexpr int kL = PST ? kLds : 0;
+    constexpr int kStg = PST ? expert_stg_bytes<T, BT, BF>() : 0;
     const int tot_m = p.table_count[0] * p.feat_tiles;
     const int tot_s = p.table_count[1] * p.feat_tiles;
     const int chunk_m = (tot_m + 7) >> 3, chunk_s = (tot_s + 7) >> 3;
-    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int xcd = blockIdx.x & 7;
     const int m_x = max(0, min(chunk_m, tot_m - xcd * chunk_m));
     const int s_x = max(0, min(chunk_s, tot_s - xcd * chunk_s));
     const int n_x = m_x + s_x;
-    if (j >= n_x) return;
     const int nk = (int)((size_t)p.K * sizeof(T) / RB);
     // the j-th tile of this XCD is large-list entry a0 when a1 > a0, else small entry j - a0
-    const int a0 = (int)((long long)j * m_x / n_x), a1 = (int)((long long)(j + 1) * m_x / n_x);
-    if (a1 > a0) {
-        const int L = xcd * chunk_m + a0;
-        const int4 te = p.table[L / p.feat_tiles];
-        const int expert = te.x, first = te.y, seg0 = te.z, segn = te.w;
-        const int n_e = (segn + BT - 1) / BT;
-        const int q = L - p.feat_tiles * first;
-        const int gtok = p.gather ? kGroupTokGather : (p.group_tok > 0 ? p.group_tok : kGroupTok);
-        const int blk_tiles = gtok * p.feat_tiles;
-        const int blk = min(q / blk_tiles, (n_e - 1) / gtok);
-        const int width = min(gtok, n_e - blk * gtok);
-        const int ql = q - blk * blk_tiles;
-        const int ftile = ql / width;
-        const int ttile = blk * gtok + (ql - ftile * width);
-        const int row0 = seg0 + ttile * BT, row_end = min(seg0 + segn, p.act_rows);
-        // keyed on the position (128-row block, feature block of the usual width) rather
-        // than the tile index, so tiles of every height sum each output in the same order
-        constexpr int kFeatUnit = NB == 2 ? kExpertUpBF : kExpertDownBF;
-        const int rblk = ttile * BT / 128, fblk = ftile * BF / kFeatUnit;
-        const int rot = kRotate && tot_s > 0 ? ((rblk + 7 * fblk) % kRotPeriod) * nk / kRotPeriod : 0;
-        if (row_end - row0 >= BT)
-            compute_tile<T, NB, EPI, BT, BF, S, RB, true, false, WKM>(p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot);
-        else
-            compute_tile<T, NB, EPI, BT, BF, S, RB, false, false, WKM>(p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot);
-    } else if constexpr (kSmallBTok > 0) {
-        constexpr int SB = kSmallBTok > 0 ? kSmallBTok : 64;
-        const int Ls = xcd * chunk_s + (j - a0);
-        const int4 te = p.stable[Ls / p.feat_tiles];
-        const int ftile = Ls - (Ls / p.feat_tiles) * p.feat_tiles;
-        const int row0 = te.z, row_end = min(te.z + te.w, p.act_rows);
-        if (row_end - row0 >= SB)
-            compute_tile<T, NB, EPI, SB, BF, kSmallStages, RB, true, true, WKM>(p, lds, te.x, row0, row_end, ftile * BF, 0, nk);
-        else
-            compute_tile<T, NB, EPI, SB, BF, kSmallStages, RB, false, true, WKM>(p, lds, te.x, row0, row_end, ftile * BF, 0, nk);
+    const int w = PST ? (int)(gridDim.x >> 3) : 0;
+    auto run = [&](int j, volatile lds_int* note) {
+        const int a0 = (int)((long long)j * m_x / n_x), a1 = (int)((long long)(j + 1) * m_x / n_x);
+        if (a1 > a0) {
+            const int L = xcd * chunk_m + a0;
+            const int4 te = p.table[L / p.feat_tiles];
+            const int expert = te.x, first = te.y, seg0 = te.z, segn = te.w;
+            const int n_e = (segn + BT - 1) / BT;
+            const int q = L - p.feat_tiles * first;
+            const int gtok = p.gather ? kGroupTokGather : (p.group_tok > 0 ? p.group_tok : kGroupTok);
+            const int blk_tiles = gtok * p.feat_tiles;
+            const int blk = min(q / blk_tiles, (n_e - 1) / gtok);
+            const int width = min(gtok, n_e - blk * gtok);
+            const int ql = q - blk * blk_tiles;
+            const int ftile = ql / width;
+            const int ttile = blk * gtok + (ql - ftile * width);
+            const int row0 = seg0 + ttile * BT, row_end = min(seg0 + segn, p.act_rows);
+            // keyed on the position (128-row block, feature block of the usual width) rather
+            // than the tile index, so tiles of every height sum each output in the same order
+            constexpr int kFeatUnit = NB == 2 ? kExpertUpBF : kExpertDownBF;
+            const int rblk = ttile * BT / 128, fblk = ftile * BF / kFeatUnit;
+            const int rot = kRotate && tot_s > 0 ? ((rblk + 7 * fblk) % kRotPeriod) * nk / kRotPeriod : 0;
+            if (row_end - row0 >= BT)
+                compute_tile<T, NB, EPI, BT, BF, S, RB, true, false, WKM, false, kL, kStg>(
+                    p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot, note, p.claim + xcd, w);
+            else
+                compute_tile<T, NB, EPI, BT, BF, S, RB, false, false, WKM, false, kL, kStg>(
+                    p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot, note, p.claim + xcd, w);
+        } else if constexpr (kSmallBTok > 0) {
+            constexpr int SB = kSmallBTok > 0 ? kSmallBTok : 64;
+            const int Ls = xcd * chunk_s + (j - a0);
+            const int4 te = p.stable[Ls / p.feat_tiles];
+            const int ftile = Ls - (Ls / p.feat_tiles) * p.feat_tiles;
+            const int row0 = te.z, row_end = min(te.z + te.w, p.act_rows);
+            if (row_end - row0 >= SB)
+                compute_tile<T, NB, EPI, SB, BF, kSmallStages, RB, true, true, WKM, false, kL, kStg>(
+                    p, lds, te.x, row0, row_end, ftile * BF, 0, nk, 0, note, p.claim + xcd, w);
+            else
+                compute_tile<T, NB, EPI, SB, BF, kSmallStages, RB, false, true, WKM, false, kL, kStg>(
+                    p, lds, te.x, row0, row_end, ftile * BF, 0, nk, 0, note, p.claim + xcd, w);
+        }
+    };
+    if constexpr (PST) {
+        __shared__ int next_tile;
+        volatile lds_int* next = (volatile lds_int*)&next_tile;
+        const bool claimer = threadIdx.x == 4 * 64;          // lane 0 of the first loader wave
+        int j = blockIdx.x >> 3;
+        while (j < n_x) {
+            run(j, claimer ? next : nullptr);
+            asm volatile("" ::: "memory");                    // read after the tile's barriers
+            j = *next;                                        // written before the last one
+        }
+    } else {
+        const int j = blockIdx.x >> 3;
+        if (j < n_x) run(j, nullptr);
     }
 }
 
@@ -721,7 +819,8 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, 
 // (expert, index of its first entry, first row, rows); an expert with 1..small rows gets
 // one `stable` entry (expert, its index, first row, rows).  count[0], count[1] = entries.
 // Segments are clipped to [0, rows) so malformed offsets can never address past the
-// buffers, and no more than cap (table) or E (stable) entries are written.  Single
+// buffers, and no more than cap (table) or E (stable) entries are written.  The persistent
+// grid's tile counters (count[kClaimUp ..]) are cleared.  Single
 // workgroup; E <= 1024.
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets, int E, int rows,
                                                           int btok, int small, int cap,
@@ -754,6 +853,7 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* offsets
         count[0] = min((int)(incl & 0xffffffff), cap);
         count[1] = (int)(incl >> 32);
     }
+    if (e < kClaimWords) count[kClaimUp + e] = 0;
 }
 
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB>
@@ -767,11 +867,23 @@ hipError_t launch_dense(const GemmParams<T, NB>& p, int grid, hipStream_t s) {
 // The grid covers the most (token tile, feature tile) items the two lists can hold
 // together, max_items = tiles_cap x feature tiles: an expert adds at most one tile beyond
 // its rows / BT, whichever list it is in.  XCD x runs ceil(m / 8) + ceil(s / 8) items of
-// the m and s that exist, at most max_items / 8 + 2.
+// the m and s that exist, at most max_items / 8 + 2.  A persistent grid (bf16, see
+// kPersist) has one workgroup per CU, or fewer when the upper bound is lower.
 template <typename T, int NB, int EPI, int BT, int BF, int S, int RB, bool WKM = false>
 hipError_t launch_expert(const GemmParams<T, NB>& p, int max_items, hipStream_t s) {
-    const int grid = 8 * ((max_items + 7) / 8 + 2);
+    int grid = 8 * ((max_items + 7) / 8 + 2);
     if (grid <= 0) return hipSuccess;
+    if constexpr (kPersist && !WKM && sizeof(T) == 2 && expert_run_fits<T, NB, BT, BF, S, RB>()) {
+        if (p.claim == nullptr) return hipErrorInvalidValue;
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return hipErrorInvalidDevice;
+        grid = min(grid, 8 * max(cus / 8, 1));
+        hipLaunchKernelGGL((expert_gemm_kernel<T, NB, EPI, BT, BF, S, RB, WKM, true>), dim3(grid),
+                           dim3(kThreads), 0, s, p);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((expert_gemm_kernel<T, NB, EPI, BT, BF, S, RB, WKM>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
@@ -923,6 +1035,7 @@ hipError_t grouped_tiles(int N, int E, int H, int F, const void* xd, const int32
     up.table = tl.table;
     up.stable = tl.stable;
     up.table_count = tl.count;
+    up.claim = tl.count + kClaimUp;
     up.out = h;
     up.out2 = a;
     up.out3 = g;
@@ -945,6 +1058,7 @@ hipError_t grouped_tiles(int N, int E, int H, int F, const void* xd, const int32
     dn.table = tl.table;
     dn.stable = tl.stable;
     dn.table_count = tl.count;
+    dn.claim = tl.count + kClaimDown;
     dn.group_tok = kGroupTokDown;
     dn.out = y;
     return launch_expert<T, 1, kEpiStore, BT, DN_BF, STAGES, RB>(
@@ -1017,6 +1131,7 @@ hipError_t grouped_pair_t(int N, int E, int H, int F, const void* act, const int
     q.table = tl.table;
     q.stable = tl.stable;
     q.table_count = tl.count;
+    q.claim = tl.count + kClaimUp;
     q.out = a;
     q.out2 = g;
     return launch_expert<T, 2, kEpiPair, BT, BF, STAGES, RB>(q, tl.cap * q.feat_tiles, s);

@@ -15,7 +15,7 @@ namespace moe {
 // (expert, index of its first entry, first row, rows); experts with 1..small rows one
 // `stable` entry; count[0], count[1] = entries (table entries capped at cap).
 struct TileTables {
-    int* count;
+    int* count;             // [0], [1]: entries; [kClaimUp, kClaimUp + kClaimWords): see below
     int4* table;
     int4* stable;
     int cap;
@@ -23,6 +23,10 @@ struct TileTables {
     int small;
 };
 TileTables gemm_tables(void* ws, long long N, int E, int F);
+// Words of the table header after the entry counts: the per-XCD tile counters of the
+// persistent expert grid, 8 for the up product from kClaimUp and 8 for the down product
+// from kClaimDown, set to 0 by whichever kernel writes the tables.
+constexpr int kClaimUp = 16, kClaimDown = 24, kClaimWords = 16;
 
 // Gate logits x.Wg^T as gate_splits() fp32 partial sums over K splits, [split][T][E] in
 // `partials` (no bias).  *zero_word (may be NULL) and zero_buf[0, zero_n) are set to 0 by

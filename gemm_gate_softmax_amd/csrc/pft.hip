@@ -332,6 +332,7 @@ __global__ __launch_bounds__(kPlaceThreads) void pft_place_kernel(
                 tt.count[0] = min(tot_m, tt.cap);
                 tt.count[1] = tot_s;
             }
+            if (tid < kClaimWords) tt.count[kClaimUp + tid] = 0;   // persistent grid's counters
         }
     }
     __syncthreads();
