@@ -42,6 +42,8 @@ enum Epilogue { kEpiLogits = 0, kEpiSwiGLU = 1, kEpiStore = 2, kEpiPair = 3, kEp
 // still fill the chip.  The macros exist to build variants for measurement.
 #ifndef MOE_SMALL_BTOK
 #define MOE_SMALL_BTOK 64      // 0: no small tiles
+#endif
+#ifndef MOE_SMALL_STAGES
 #define MOE_SMALL_STAGES 3
 #endif
 #ifndef MOE_EXPERT_BTOK
@@ -94,6 +96,14 @@ constexpr bool kInterleave = MOE_INTERLEAVE_READS != 0;
 #endif
 constexpr bool kRotate = MOE_K_ROTATE != 0;
 constexpr int kRotPeriod = MOE_K_ROTATE > 0 ? MOE_K_ROTATE : 1;
+// Products with one weight operand (the down product, the backward's dh and dxd) rotate
+// only with MOE_K_ROTATE_DOWN=1: with the persistent tile loop the down product ran faster
+// without it (fused layer at X-MoE Large, rotated / not: 4.005 / 3.970 ms and 4.011 / 3.973
+// ms in two alternating rounds; X-MoE Small level).
+#ifndef MOE_K_ROTATE_DOWN
+#define MOE_K_ROTATE_DOWN 0
+#endif
+constexpr bool kRotateDown = MOE_K_ROTATE_DOWN != 0;
 // Experts with at most kSmallBTok rows get one small tile: kSmallBTok tokens, the same
 // features, a kSmallStages-slot ring.  Such a tile is mostly a weight stream; in its own
 // list it can be spread evenly among the MFMA-heavy tiles of the large experts, and its
@@ -777,7 +787,8 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, 
             // than the tile index, so tiles of every height sum each output in the same order
             constexpr int kFeatUnit = NB == 2 ? kExpertUpBF : kExpertDownBF;
             const int rblk = ttile * BT / 128, fblk = ftile * BF / kFeatUnit;
-            const int rot = kRotate && tot_s > 0 ? ((rblk + 7 * fblk) % kRotPeriod) * nk / kRotPeriod : 0;
+            const bool rotate = kRotate && (NB == 2 || kRotateDown) && tot_s > 0;
+            const int rot = rotate ? ((rblk + 7 * fblk) % kRotPeriod) * nk / kRotPeriod : 0;
             if (row_end - row0 >= BT)
                 compute_tile<T, NB, EPI, BT, BF, S, RB, true, false, WKM, false, kL, kStg>(
                     p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot, note, p.claim + xcd, w);

@@ -3,8 +3,8 @@
 The up product at X-MoE Large runs at the memory fabric's cap, so its time follows the bytes
 that miss the L2s.  This model replays a launch's tiles the way ``expert_gemm_kernel`` orders
 them (the two tile lists, each XCD's contiguous share of both interleaved evenly, large
-experts' token tiles in blocks with the feature tile slowest, the K rotation keyed on the
-tile's position) on 8 XCDs of 32 CUs each.  Every CU runs one tile at a time and steps
+experts' token tiles in blocks with the feature tile slowest, the up product's K rotation
+keyed on the tile's position) on 8 XCDs of 32 CUs each.  Every CU runs one tile at a time and steps
 through its k-slices at a fixed rate (a per-tile factor drawn from [1 - jitter, 1 + jitter]
 stands in for the spread of real tile times); each k-slice requests its operand blocks
 (one 16-byte-per-lane slice of the activation rows, one of each weight operand) from the
@@ -146,7 +146,8 @@ def simulate(counts, *, n_feat: int, nk: int, nb: int = 2, bt: int = 128, bf: in
 def variants(cfg):
     """The kept schedule of each product and the alternatives weighed against it."""
     up = dict(n_feat=cfg.F, nk=cfg.H * 2 // ROW_BYTES)
-    down = dict(n_feat=cfg.H, nk=cfg.F * 2 // ROW_BYTES, nb=1, bf=256, feat_unit=256)
+    down = dict(n_feat=cfg.H, nk=cfg.F * 2 // ROW_BYTES, nb=1, bf=256, feat_unit=256,
+                rotate=False)
     return [
         ("up, kept: 128 x (2 x 128), blocks of 32, rotation", up),
         ("up, no K rotation", dict(up, rotate=False)),
@@ -158,7 +159,8 @@ def variants(cfg):
         ("up, blocks of 16 token tiles", dict(up, group=16)),
         ("up, 128 x (2 x 256) tiles", dict(up, bf=256, t_large=2.0, t_small=1.8)),
         ("up, 256 x (2 x 128) tiles", dict(up, bt=256, t_large=2.0)),
-        ("down, kept: 128 x 256, blocks of 32, rotation", down),
+        ("down, kept: 128 x 256, blocks of 32, no rotation", down),
+        ("down, K rotation", dict(down, rotate=True)),
     ]
 
 

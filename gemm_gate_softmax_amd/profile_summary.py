@@ -197,7 +197,8 @@ def steps_markdown(a):
         out.append(f"| {p} | `{name}` | {d:.1f} | {g:.1f} |")
     span = med([(st[-1][2] - st[0][1]) / 1e3 for st in steps])
     busy = med([sum(e - b for _, b, e in st) / 1e3 for st in steps])
-    out += ["", f"Step span {span:.1f} us: kernels {busy:.1f} us, gaps {span - busy:.1f} us "
+    gaps = max(span - busy, 0.0)            # (rounding of the medians can dip below 0)
+    out += ["", f"Step span {span:.1f} us: kernels {busy:.1f} us, gaps {gaps:.1f} us "
             f"({len(shape)} dispatches)."]
     return "\n".join(out) + "\n"
 
