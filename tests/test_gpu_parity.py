@@ -361,6 +361,50 @@ def test_layer_parity_small(orc, cfg):
     assert int(host(ws[:4].view(torch.int32))[0]) == 0
 
 
+# Layers with more tiles than the chip has CUs in both bf16 expert products, so their
+# persistent tile loop runs several tiles per workgroup, claimed from the per-XCD counters,
+# with the 64-token tiles of small experts mixed among the 128-token tiles.  The second draw
+# runs on the first call's workspace, whose counters the first call left at their final
+# values: the kernel that writes the tile tables has to clear them.  The first draw gathers
+# its rows from x (dispatch fused), the second reads them from xd.
+RUN_LAYERS = [
+    W.LayerConfig("runs_bf16", T=2048, H=1024, E=48, F=1024, k=4, dtype="bf16", bias=("zipf", 1.2)),
+    W.LayerConfig("runs_skew_bf16", T=1536, H=512, E=40, F=768, k=3, dtype="bf16", bias=("zipf", 1.2)),
+]
+
+
+@pytest.mark.parametrize("cfg", RUN_LAYERS, ids=lambda c: c.name)
+def test_layer_persistent_runs(orc, cfg):
+    dt = cfg.dtype
+    ws = None
+    for seed in (0, 1):
+        d = W.make_host(cfg, seed=seed)
+        out, bufs, ws = ops.moe_layer_forward(dev(d["x"], dt), dev(d["wg"], dt), dev(d["bias"]),
+                                              dev(d["w1"], dt), dev(d["w3"], dt), dev(d["w2"], dt),
+                                              cfg.k, ws=ws, fuse_dispatch=seed == 0)
+        assert (bufs["xd"] is None) == (seed == 0)
+        te_ref, tw_ref, _, l64 = orc.gate_topk(dt, d["x"], d["wg"], d["bias"], cfg.k, want_logits=True)
+        r = compare_routing(host(bufs["top_experts"]), te_ref, l64, cfg.k)
+        assert len(r["mismatch"]) == 0
+        b_ref = orc.pft_build(te_ref, cfg.E)
+        for n in ("counts", "offsets", "token_ids", "expert_ids", "dest_pos"):
+            assert np.array_equal(host(bufs[n]), b_ref[n]), n
+        c = b_ref["counts"]
+        tiles = int(sum((n + 127) // 128 for n in c if n > 64) + np.count_nonzero((c > 0) & (c <= 64)))
+        # more up-product tiles than CUs (runs_bf16: the down product's too), small experts among them
+        assert tiles * (cfg.F // 128) > 256 and np.any((c > 0) & (c <= 64))
+        xd_ref = orc.dispatch(dt, d["x"], b_ref["dest_pos"])
+        h_ref, y_ref = orc.grouped_gemm_swiglu(dt, xd_ref, b_ref["offsets"], d["w1"], d["w3"], d["w2"])
+        out_ref = orc.combine(dt, y_ref, b_ref["dest_pos"], tw_ref)
+        eh = max_abs_rel(host(bufs["h"], dt), h_ref, dt)
+        ey = max_abs_rel(host(bufs["y"], dt), y_ref, dt)
+        eo = max_abs_rel(host(out, dt), out_ref, dt)
+        _log(f"persistent runs {cfg.name} seed {seed}: {tiles} token tiles x {cfg.F // 128} up / "
+             f"{cfg.H // 256} down feature tiles; err h {eh:.2e} y {ey:.2e} out {eo:.2e}")
+        assert eh <= TOL[dt] and ey <= TOL[dt] and eo <= TOL[dt]
+        assert ws_word(ws, 0) == 0
+
+
 # The method's degenerate layers: one expert (every token to it with weight 1: a dense
 # SwiGLU FFN), every expert chosen by every token (k = E), and a single token.
 DEGENERATE_LAYERS = [
