@@ -86,6 +86,9 @@ def parse():
                          "--variant): the fused layer, its up product and both expert products "
                          "timed with each, alternating, outputs compared with the first's")
     ap.add_argument("--ab-reps", type=int, default=3)
+    ap.add_argument("--ab-backward", action="store_true",
+                    help="with --ab: also time moe_layer_backward with each build and compare its "
+                         "gradients with the first build's")
     ap.add_argument("--memory-ceilings", action="store_true",
                     help="read rates of the loads the tile engine issues (libmoe_probe.so): "
                          "direct-to-LDS and plain, 4 and 8 issuing waves per CU, from regions "
@@ -419,6 +422,18 @@ def ab_compare(cfg, args, dev):
                                      top_weights=tw, ws=gate_ws)
     ref, res = None, {p: {"layer": [], "up": [], "experts": [], "gate": []} for p in libs}
     agree = {}
+    bwd = {"grads": None, "ws": None, "ref": None, "dout": None, "agree": {}}
+    if args.ab_backward:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed + 1)
+        bwd["dout"] = torch.randn((cfg.T, cfg.H), generator=gen, device=dev).to(d["x"].dtype)
+        for p in libs:
+            res[p]["backward"] = []
+
+    def backward():
+        bwd["grads"], bwd["ws"] = ops.moe_layer_backward(
+            d["x"], d["wg"], d["bias"], d["w1"], d["w3"], d["w2"], cfg.k, bufs, bwd["dout"],
+            grads=bwd["grads"], ws=bwd["ws"])
     for _ in range(max(1, args.ab_reps)):
         for p in libs:
             use(p)
@@ -431,15 +446,30 @@ def ab_compare(cfg, args, dev):
                 same = all(torch.equal(got[n], ref[n]) for n in got)
                 err = max(float((got[n] - ref[n]).abs().max() / ref[n].abs().max()) for n in got)
                 agree[p] = "bit-identical" if same else f"max-abs-rel {err:.2e}"
+            if args.ab_backward and p not in bwd["agree"]:
+                backward()                       # on this build's forward intermediates
+                torch.cuda.synchronize()
+                g = {n: t.clone() for n, t in bwd["grads"].items() if t is not None}
+                if bwd["ref"] is None:
+                    bwd["ref"] = g
+                bwd["agree"][p] = "bit-identical" if all(
+                    torch.equal(g[n], bwd["ref"][n]) for n in g) else "differs"
+                del g
             for name, fn in (("layer", layer), ("up", up), ("experts", both), ("gate", gate)):
                 fn()
                 torch.cuda.synchronize()
                 res[p][name].append(time_steps(fn, 10, stream)["median"])
+            if args.ab_backward:
+                layer()                          # the intermediates the backward reads
+                backward()
+                torch.cuda.synchronize()
+                res[p]["backward"].append(time_steps(backward, 3, stream)["median"])
             log(f"ab {cfg.name} {os.path.basename(p)}: layer {res[p]['layer'][-1]:.3f} ms, up "
                 f"{res[p]['up'][-1]:.3f} ms, both products {res[p]['experts'][-1]:.3f} ms, gate "
                 f"{res[p]['gate'][-1] * 1e3:.1f} us")
     print(json.dumps({"ab": cfg.name, "libs": [
         {"lib": os.path.relpath(p, ROOT), "outputs_vs_first": agree[p],
+         **({"gradients_vs_first": bwd["agree"][p]} if args.ab_backward else {}),
          **{f"{n}_ms_min": round(min(v), 4) for n, v in res[p].items()}} for p in libs]}),
         flush=True)
     return 0
