@@ -15,8 +15,11 @@ checks the three properties the kernel relies on:
 import pytest
 
 
-def loader_schedule(S, nk, c):
-    """Events of one loader wave: ("issue", stage, slot) per transfer, ("wait", n), ("barrier", b)."""
+def loader_schedule(S, nk, c, pre=None):
+    """Events of one loader wave: ("issue", stage, slot) per transfer, ("wait", n), ("barrier", b).
+    pre: stages issued before barrier 0 (S - 1, or fewer in a persistent run of tiles, where
+    the rest follow barrier 0)."""
+    pre = S - 1 if pre is None else pre
     ev = []
 
     def issue(stage, slot):
@@ -26,9 +29,11 @@ def loader_schedule(S, nk, c):
         issue(0, 0)
         ev += [("wait", 0), ("barrier", 0)]
     else:
-        for s in range(S - 1):
+        for s in range(pre):
             issue(min(s, nk - 1), s)
-        ev += [("wait", (S - 2) * c), ("barrier", 0)]
+        ev += [("wait", (pre - 1) * c), ("barrier", 0)]
+        for s in range(pre, S - 1):
+            issue(min(s, nk - 1), s)
     refill = S - 1
     for kt in range(nk - 1):
         if kt + S - 1 < nk:
@@ -44,11 +49,11 @@ def loader_schedule(S, nk, c):
     return ev
 
 
-def check(S, nk, c):
+def check(S, nk, c, pre=None):
     issued = []          # (stage, slot) per transfer, in issue order
     landed = 0           # transfers retired (in order)
     last_barrier = -1    # compute waves read slice b between barriers b and b + 1
-    for e in loader_schedule(S, nk, c):
+    for e in loader_schedule(S, nk, c, pre):
         if e[0] == "issue":
             _, stage, slot = e
             # the slot must not hold a slice the compute waves may still read: the slice in
@@ -85,6 +90,16 @@ def test_loader_ring_counts(S):
     for nk in range(1, 61):
         for c in range(1, 13):
             check(S, nk, c)
+
+
+@pytest.mark.parametrize("S", [3, 4])
+def test_loader_ring_counts_persistent_prologue(S):
+    # a tile of a persistent run issues only its first `pre` stages before barrier 0 (the
+    # previous tile's outputs may still be staged in the others' slots) and the rest after it
+    for pre in range(1, S - 1):
+        for nk in range(1, 61):
+            for c in range(1, 13):
+                check(S, nk, c, pre)
 
 
 def test_no_redundant_transfers_once_k_covers_the_ring():
