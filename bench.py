@@ -19,7 +19,8 @@ per-stage table goes to stderr first.
   python bench.py --memory-ceilings    # how fast one workgroup per CU can read 16 bytes a
                                        # lane from the L2s, the Infinity Cache and HBM
   python bench.py --ab LIB,LIB,...     # the layer with each library (variants built by
-                                       # gemm_gate_softmax_amd.build --variant), alternating
+                                       # gemm_gate_softmax_amd.build --variant), alternating;
+                                       # --ab-backward times moe_layer_backward as well
 
 The roofline object covers the dominant kernel, the expert gate/up product with its
 SwiGLU epilogue (two thirds of the layer's flops), timed on its own through the same
