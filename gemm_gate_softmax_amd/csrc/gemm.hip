@@ -116,15 +116,16 @@ constexpr bool kRotateDown = MOE_K_ROTATE_DOWN != 0;
 constexpr int kSmallBTok = MOE_SMALL_BTOK;
 constexpr int kSmallStages = MOE_SMALL_STAGES;
 // bf16 expert products (the forward's two, and the backward's recompute of a and g and its
-// products with K-major weights, dh and dxd) run as a persistent tile loop, one workgroup per CU claiming tiles from per-XCD counters, so a
-// tile's start-up (table lookups, the first slices' latency) overlaps the previous tile's
-// epilogue (expert_gemm_kernel, PST).  Measured, fused layer, one-tile-per-workgroup grid
-// against the loop (same box, alternating): X-MoE Small 0.997 / 0.965 ms, Medium 1.743 /
-// 1.714, Large 4.117 / 4.048; the top-2 fp32 layer, whose tiles are four times longer per
-// k-slice, ran 2.243 / 2.282 ms with it, so fp32 keeps one tile per workgroup.  A static
-// schedule (tile i, i + W, ... per workgroup) instead of the counters: X-MoE Large 4.180 ms.
-// The backward's dh and dxd on the loop: layer backward 14.90 -> 14.79 / 14.83 ms at X-MoE
-// Large, 3.395 -> 3.373 ms at Small.  0 switches the loop off.
+// products with K-major weights, dh and dxd) run as a persistent tile loop, one workgroup
+// per CU claiming tiles from per-XCD counters, so a tile's start-up (table lookups, the
+// first slices' latency) overlaps the previous tile's epilogue (expert_gemm_kernel, PST).
+// Measured, fused layer, one-tile-per-workgroup grid against the loop (same box,
+// alternating): X-MoE Small 0.997 / 0.965 ms, Medium 1.743 / 1.714, Large 4.117 / 4.048;
+// the top-2 fp32 layer, whose tiles are four times longer per k-slice, ran 2.243 / 2.282 ms
+// with it, so fp32 keeps one tile per workgroup.  A static schedule (tile i, i + W, ... per
+// workgroup) instead of the counters: X-MoE Large 4.180 ms.  The backward's dh and dxd on
+// the loop: layer backward 14.90 -> 14.79 / 14.83 ms at X-MoE Large, 3.395 -> 3.373 ms at
+// Small.  0 switches the loop off.
 #ifndef MOE_PERSIST
 #define MOE_PERSIST 1
 #endif
