@@ -81,16 +81,23 @@ constexpr int kGroupTokDown = MOE_GROUP_TOK_DOWN;
 #endif
 constexpr bool kInterleave = MOE_INTERLEAVE_READS != 0;
 // In a launch that also streams small experts' weights, a large tile starts its K loop at
-// slice ((rb + 7 fb) mod P) * nk / P and wraps around (rb: its first row's 128-row block
-// within the expert, fb: its first feature's block of the usual tile width, so tiles of
-// every height sum in the same order).  There the large tiles start at staggered times as CUs
-// free up from tiles of unequal length, and tiles sharing an operand panel then line up
-// their slices in L2 more often; without small tiles, tiles start and run together and the
-// natural order shares best.  The start depends only on the tile, so a gathered
-// (fused-dispatch) product and one reading xd sum in the same order.  Measured (fused layer,
-// on / off): X-MoE Large 4.19 / 4.25 ms, X-MoE Super 5.27 / 5.33 ms; X-MoE Medium (no small
-// experts) 1.81 / 1.77 ms and dense products up to 30% slower with it, hence the
-// condition.  P = 16 and 64 read more and ran slower at X-MoE Large; 0 switches it off.
+// slice ((rb + w fb) mod P) * nk / P and wraps around (rb: its first row's 128-row block
+// within the expert, fb: its first feature's block of the usual tile width, w: the expert's
+// count of 128-row blocks capped at 32, so tiles of every height sum in the same order).
+// There the large tiles start at staggered times as CUs free up from tiles of unequal
+// length, one tile every nk / P slices or so per XCD; tiles go out in blocks of up to 32
+// token tiles with the feature tile slowest, so a tile's neighbour in the token direction
+// starts about nk / P slices later and its neighbour in the feature direction about w nk / P
+// later, and with those offsets both read the same slices at about the same time, which
+// lets them share operand slices in L2; without small tiles, tiles start and run together
+// and the natural order shares best.  The start depends only on the tile and its expert's
+// row count, so a gathered (fused-dispatch) product and one reading xd sum in the same
+// order.  Measured (fused layer, on / off): X-MoE Large 4.19 / 4.25 ms, X-MoE Super 5.27 /
+// 5.33 ms; X-MoE Medium (no small experts) 1.81 / 1.77 ms and dense products up to 30%
+// slower with it, hence the condition.  P = 16 and 64 read more and ran slower at X-MoE
+// Large; 0 switches it off.  A fixed feature step of 7 in place of w (tuned for blocks of 8
+// token tiles): up product 2.544 / 2.527 ms and 2.546 / 2.527 ms (7 / w) at X-MoE Large,
+// 0.564 / 0.559 ms at Small, 3.181 / 3.166 ms at Super.
 #ifndef MOE_K_ROTATE
 #define MOE_K_ROTATE 32
 #endif
@@ -790,7 +797,8 @@ __global__ __launch_bounds__(kThreads, 1) void expert_gemm_kernel(GemmParams<T, 
             constexpr int kFeatUnit = NB == 2 ? kExpertUpBF : kExpertDownBF;
             const int rblk = ttile * BT / 128, fblk = ftile * BF / kFeatUnit;
             const bool rotate = kRotate && (NB == 2 || kRotateDown) && tot_s > 0;
-            const int rot = rotate ? ((rblk + 7 * fblk) % kRotPeriod) * nk / kRotPeriod : 0;
+            const int fstep = min((segn + 127) / 128, 32);
+            const int rot = rotate ? ((rblk + fstep * fblk) % kRotPeriod) * nk / kRotPeriod : 0;
             if (row_end - row0 >= BT)
                 compute_tile<T, NB, EPI, BT, BF, S, RB, true, false, WKM, false, kL, kStg>(
                     p, lds, expert, row0, row_end, ftile * BF, 0, nk, rot, note, p.claim + xcd, w);

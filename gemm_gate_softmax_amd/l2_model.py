@@ -88,8 +88,9 @@ def simulate(counts, *, n_feat: int, nk: int, nb: int = 2, bt: int = 128, bf: in
              epilogue: float = 2.3, jitter: float = 0.0, seed: int = 0,
              l2_bytes: int = L2_BYTES) -> tuple[int, int]:
     """(bytes missing the L2s, bytes requested) over one launch.  Times are in k-slices of
-    a large tile.  rot_key: the rotation's key, "pos" (rb + 7 fb, as the kernel), "rb" (token
-    block only) or "fb" (feature block only)."""
+    a large tile.  rot_key: the rotation's key, "pos" (rb + w fb, w the expert's 128-row
+    blocks capped at 32, as the kernel), "pos7" (rb + 7 fb), "rb" (token block only) or "fb"
+    (feature block only)."""
     rng = np.random.default_rng(seed)
     feat_tiles = (n_feat + bf - 1) // bf
     large, smalls = tile_lists(counts, bt, feat_tiles, group)
@@ -111,7 +112,9 @@ def simulate(counts, *, n_feat: int, nk: int, nb: int = 2, bt: int = 128, bf: in
             rot = 0
             if is_large and rot_on:
                 rblk, fblk = tt * bt // 128, ft * bf // feat_unit
-                key = {"pos": rblk + 7 * fblk, "rb": rblk, "fb": 7 * fblk}[rot_key]
+                wdt = min((int(counts[e]) + 127) // 128, 32)
+                key = {"pos": rblk + wdt * fblk, "pos7": rblk + 7 * fblk, "rb": rblk,
+                       "fb": wdt * fblk}[rot_key]
                 rot = (key % rot_period) * nk // rot_period
             f = 1.0 + jitter * (2.0 * rng.random() - 1.0)
             heapq.heappush(heap, (t + prologue * f, cu, is_large, e, tt, ft, rows, 0, rot, f))
@@ -151,6 +154,7 @@ def variants(cfg):
     return [
         ("up, kept: 128 x (2 x 128), blocks of 32, rotation", up),
         ("up, no K rotation", dict(up, rotate=False)),
+        ("up, rotation step 7 in the feature direction", dict(up, rot_key="pos7")),
         ("up, rotation keyed on the token block", dict(up, rot_key="rb")),
         ("up, rotation keyed on the feature block", dict(up, rot_key="fb")),
         ("up, rotation period 16", dict(up, rot_period=16)),
