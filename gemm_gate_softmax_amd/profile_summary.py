@@ -189,11 +189,11 @@ def steps_markdown(a):
     out = [f"# {a.title}", "", "Command (repository root, one MI355X):", "", f"    {a.command}", "",
            f"The last {len(steps)} layer steps of the run (dispatches from `{a.first}` through "
            f"`{a.last}`), medians over the steps; a gap is the time from the end of the previous "
-           "dispatch to the start of this one.", "",
+           "dispatch to the start of this one (0 when they overlap).", "",
            "| # | kernel | duration (us) | gap before (us) |", "|---|---|---|---|"]
     for p, name in enumerate(shape):
         d = med([(st[p][2] - st[p][1]) / 1e3 for st in steps])
-        g = med([(st[p][1] - st[p - 1][2]) / 1e3 for st in steps]) if p else 0.0
+        g = max(med([(st[p][1] - st[p - 1][2]) / 1e3 for st in steps]), 0.0) if p else 0.0
         out.append(f"| {p} | `{name}` | {d:.1f} | {g:.1f} |")
     span = med([(st[-1][2] - st[0][1]) / 1e3 for st in steps])
     busy = med([sum(e - b for _, b, e in st) / 1e3 for st in steps])

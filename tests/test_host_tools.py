@@ -103,6 +103,18 @@ def test_layer_steps_durations_and_gaps(tmp_path):
     assert "Step span 27.0 us: kernels 22.0 us, gaps 5.0 us" in md
 
 
+def test_layer_steps_overlapping_kernels_report_no_negative_gap(tmp_path):
+    # the second kernel starts 10 ns before the first ends (the trace's clocks allow it):
+    # the kernels' summed time exceeds the step's span, and the gap total stays at 0
+    rows = [{"Kernel_Name": "first_k(int)", "Start_Timestamp": 0, "End_Timestamp": 5000},
+            {"Kernel_Name": "last_k(int)", "Start_Timestamp": 4990, "End_Timestamp": 9990}]
+    trace = _csv(tmp_path / "t.csv", rows)
+    a = argparse.Namespace(trace=trace, first="first_k", last="last_k", exclude=None,
+                           last_steps=20, title="t", command="c")
+    md = ps.steps_markdown(a)
+    assert "Step span 10.0 us: kernels 10.0 us, gaps 0.0 us" in md and "-0.0" not in md
+
+
 def test_counter_means_sum_instances_and_average_last_dispatches(tmp_path):
     k = "void expert_gemm_kernel<moe::bf16_t, 2, 1, 128, 128, 3, 128, false>(...)"
     rows = []
